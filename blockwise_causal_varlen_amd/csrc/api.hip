@@ -1,0 +1,717 @@
+// Host side of the C ABI declared in include/attn.h: argument validation,
+// workspace sizing, kernel selection by shape, and the virtual-rank schedule
+// drivers (zig-zag ring, contiguous ring, KV-parallel). No entry point reads
+// device memory on the host or synchronises, except attn_validate_inputs.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "internal.h"
+
+using namespace attn;
+
+namespace {
+
+thread_local std::string g_err;
+
+attn_status fail(attn_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+attn_status ok() { return ATTN_OK; }
+
+attn_status hip_check(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TRY(x)                        \
+  do {                                \
+    attn_status _s = (x);             \
+    if (_s != ATTN_OK) return _s;     \
+  } while (0)
+
+int esize(int32_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+// A tensor descriptor with [n_tok, n_head, head_dim], 16-byte aligned rows.
+attn_status check_tensor(const attn_tensor *t, const char *name, bool allow_f32 = true) {
+  if (!t) return fail(ATTN_ERR_NULL, "%s: descriptor is NULL", name);
+  if (!t->data && t->n_tok > 0) return fail(ATTN_ERR_NULL, "%s: data is NULL", name);
+  if (t->dtype != ATTN_BF16 && !(allow_f32 && t->dtype == ATTN_F32))
+    return fail(ATTN_ERR_DTYPE, "%s: unsupported dtype %d", name, t->dtype);
+  if (t->n_tok < 0 || t->n_head <= 0 || t->head_dim <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: bad sizes [%lld, %lld, %lld]", name, (long long)t->n_tok,
+                (long long)t->n_head, (long long)t->head_dim);
+  if (t->stride_tok <= 0 || t->stride_head <= 0)
+    return fail(ATTN_ERR_LAYOUT, "%s: strides must be positive", name);
+  const int64_t eb = esize(t->dtype);
+  if (((uintptr_t)t->data) % 16 || (t->stride_tok * eb) % 16 || (t->stride_head * eb) % 16)
+    return fail(ATTN_ERR_LAYOUT, "%s: data and row strides must be 16-byte aligned", name);
+  if (t->stride_head < t->head_dim && t->n_head > 1 && t->stride_tok < t->head_dim)
+    return fail(ATTN_ERR_LAYOUT, "%s: rows overlap", name);
+  return ok();
+}
+
+attn_status check_hd(int64_t d) {
+  if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head_dim %lld not supported (64 or 128)", (long long)d);
+  return ok();
+}
+
+attn_status check_mask(const attn_mask *m) {
+  if (!m) return ok();
+  if (m->struct_size != sizeof(attn_mask))
+    return fail(ATTN_ERR_VERSION, "attn_mask.struct_size %u != %zu (header/library mismatch)", m->struct_size,
+                sizeof(attn_mask));
+  if (m->q_view > 2 || m->k_view > 2) return fail(ATTN_ERR_INVALID, "bad view %u/%u", m->q_view, m->k_view);
+  if (m->window < 0) return fail(ATTN_ERR_INVALID, "window must be >= 0");
+  if (m->kv_interleave < 0) return fail(ATTN_ERR_INVALID, "kv_interleave must be >= 0");
+  if (m->kv_interleave > 0 && (m->block_size <= 0 || m->kv_rank < 0 || m->kv_rank >= m->kv_interleave))
+    return fail(ATTN_ERR_INVALID, "round robin needs block_size > 0 and 0 <= kv_rank < kv_interleave");
+  if (m->block_table && (m->block_size <= 0 || m->max_blocks <= 0 || m->page_stride <= 0))
+    return fail(ATTN_ERR_INVALID, "paged keys need block_size, max_blocks and page_stride > 0");
+  if (m->seg_size < 0) return fail(ATTN_ERR_INVALID, "seg_size must be >= 0");
+  if (m->seg_size > 0 && m->q_view != ATTN_VIEW_ALL)
+    return fail(ATTN_ERR_UNSUPPORTED, "segments with a q view are not supported");
+  return ok();
+}
+
+MaskDev mask_dev(const attn_mask *m) {
+  MaskDev d{};
+  if (!m) return d;
+  d.causal = m->causal ? 1 : 0;
+  d.q_view = (int32_t)m->q_view;
+  d.k_view = (int32_t)m->k_view;
+  d.seg_size = m->seg_size;
+  d.window = m->window;
+  d.q_pos_offset = m->q_pos_offset;
+  d.pm.k_pos_offset = m->k_pos_offset;
+  d.pm.interleave = m->kv_interleave;
+  d.pm.rank = m->kv_rank;
+  d.pm.block = m->block_size;
+  return d;
+}
+
+TensorDev tdev(const attn_tensor *t) { return TensorDev{t->data, t->stride_tok, t->stride_head}; }
+
+struct Problem {
+  int64_t n_q, n_k_logical, hq, hkv, d;
+  int64_t nseg;
+  bool decode;
+  bool paged;
+};
+
+attn_status check_qkv(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v) {
+  TRY(check_tensor(q, "q"));
+  TRY(check_tensor(k, "k"));
+  TRY(check_tensor(v, "v"));
+  if (k->dtype != q->dtype || v->dtype != q->dtype)
+    return fail(ATTN_ERR_DTYPE, "q/k/v dtypes differ (%d/%d/%d)", q->dtype, k->dtype, v->dtype);
+  if (k->head_dim != q->head_dim || v->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "head_dim mismatch");
+  TRY(check_hd(q->head_dim));
+  if (k->n_head != v->n_head || k->n_tok != v->n_tok) return fail(ATTN_ERR_SHAPE, "k/v shapes differ");
+  if (q->n_head % k->n_head) return fail(ATTN_ERR_GQA, "GQA mismatch: %lld q heads vs %lld kv heads",
+                                         (long long)q->n_head, (long long)k->n_head);
+  return ok();
+}
+
+attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t num_seqs,
+                     int32_t max_q, int32_t max_k, const attn_mask *m, Problem &P) {
+  TRY(check_qkv(q, k, v));
+  TRY(check_mask(m));
+  if (num_seqs < 0 || max_q < 0 || max_k < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
+  P.n_q = q->n_tok;
+  P.hq = q->n_head;
+  P.hkv = k->n_head;
+  P.d = q->head_dim;
+  P.paged = m && m->block_table;
+  P.n_k_logical = P.paged ? (int64_t)m->max_blocks * m->block_size : k->n_tok;
+  P.nseg = (m && m->seg_size > 0) ? ((int64_t)max_k + m->seg_size - 1) / m->seg_size : 0;
+  if (P.nseg == 0 && m && m->seg_size > 0) P.nseg = 1;
+  const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
+                            m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
+  P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
+  return ok();
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs) {
+  if (P.decode) return 0;
+  const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
+  size_t b = align256(sched_bytes(cap));
+  if (P.nseg > 0) {
+    b += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
+    b += align256((size_t)P.nseg * P.hq * P.n_q * 4);
+  }
+  return b;
+}
+
+size_t bwd_ws_bytes(int64_t n_q, int64_t n_k, int64_t hq, int32_t num_seqs, bool need_delta) {
+  size_t b = align256(sched_bytes(sched_capacity(n_q, num_seqs, kBwdTile, 1)));
+  b += align256(sched_bytes(sched_capacity(n_k, num_seqs, kBwdTile, 1)));
+  if (need_delta) b += align256((size_t)hq * n_q * 4);
+  return b;
+}
+
+attn_status check_out(const attn_tensor *out, const Problem &P, const char *name) {
+  TRY(check_tensor(out, name));
+  if (out->n_tok != P.n_q || out->n_head != P.hq || out->head_dim != P.d)
+    return fail(ATTN_ERR_SHAPE, "%s must be [n_q, HQ, D]", name);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char *attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "null pointer";
+    case ATTN_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case ATTN_ERR_SHAPE: return "shape mismatch";
+    case ATTN_ERR_GQA: return "q heads not a multiple of kv heads";
+    case ATTN_ERR_CU_SEQLENS: return "bad cu_seqlens / max_seqlen";
+    case ATTN_ERR_LAYOUT: return "bad layout";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP error";
+    case ATTN_ERR_VERSION: return "struct version mismatch";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_CONTENT: return "invalid device data";
+  }
+  return "unknown status";
+}
+
+const char *attn_last_error(void) { return g_err.c_str(); }
+
+attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask,
+                                size_t *bytes) {
+  if (!bytes) return fail(ATTN_ERR_NULL, "bytes is NULL");
+  TRY(check_tensor(q, "q"));
+  TRY(check_tensor(k, "k"));
+  TRY(check_mask(mask));
+  if (op == ATTN_OP_BLOCK_FWD) {
+    Problem P;
+    TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+    *bytes = fwd_ws_bytes(P, num_seqs);
+    return ok();
+  }
+  if (op == ATTN_OP_BLOCK_BWD) {
+    *bytes = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, true);
+    return ok();
+  }
+  return fail(ATTN_ERR_INVALID, "unknown op %d", (int)op);
+}
+
+attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
+                           const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  Problem P;
+  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+  TRY(check_out(out, P, "out"));
+  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = fwd_ws_bytes(P, num_seqs);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (num_seqs == 0 || P.n_q == 0) return ok();
+
+  if (P.decode) {
+    DecodeArgs a;
+    a.q = tdev(q); a.k = tdev(k); a.v = tdev(v);
+    a.head_dim = (int32_t)P.d; a.hq = (int32_t)P.hq; a.hkv = (int32_t)P.hkv; a.num_seqs = num_seqs;
+    a.scale = scale; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
+    a.lse = lse; a.lse_n = P.n_q; a.n_k = k->n_tok;
+    return hip_check(launch_decode(a, s), "decode kernel");
+  }
+
+  const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
+  char *w = (char *)workspace;
+  SchedBufs sb = sched_carve(w, cap);
+  w += align256(sched_bytes(cap));
+  MaskDev md = mask_dev(mask);
+  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM, kFwdBN, 0,
+                                (int32_t)P.nseg, sb, s), "scheduler"));
+  FwdArgs a;
+  a.q = tdev(q); a.k = tdev(k); a.v = tdev(v);
+  a.dtype = q->dtype; a.head_dim = (int32_t)P.d; a.hq = (int32_t)P.hq; a.hkv = (int32_t)P.hkv;
+  a.scale = scale; a.mask = md;
+  a.block_table = P.paged ? mask->block_table : nullptr;
+  a.block_size = mask ? mask->block_size : 0;
+  a.max_blocks = mask ? mask->max_blocks : 0;
+  a.page_stride = mask ? mask->page_stride : 0;
+  a.n_pages = P.paged ? k->n_tok / mask->block_size : 0;
+  a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
+  a.lse = lse; a.lse_n = P.n_q;
+  a.part_out = nullptr; a.part_lse = nullptr;
+  a.n_q = P.n_q;
+  a.sched = sb;
+  a.grid_items = cap;
+  if (P.nseg > 0) {
+    a.part_out = (float *)w;
+    w += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
+    a.part_lse = (float *)w;
+    // segments no tile reaches must read as empty partials
+    TRY(hip_check(launch_fill(a.part_lse, P.nseg * P.hq * P.n_q, -INFINITY, s), "fill"));
+  }
+  TRY(hip_check(launch_fwd(a, s), "forward kernel"));
+  if (P.nseg > 0) {
+    MergeNArgs mn{};
+    mn.n_parts = (int32_t)P.nseg;
+    mn.strided = 1;
+    mn.out_stride = P.n_q * P.hq * P.d;
+    mn.lse_stride = P.hq * P.n_q;
+    mn.pout[0] = a.part_out; mn.pdtype[0] = ATTN_F32; mn.p_st[0] = P.hq * P.d; mn.p_sh[0] = P.d;
+    mn.plse[0] = a.part_lse;
+    mn.out = out->data; mn.out_dtype = out->dtype; mn.o_st = out->stride_tok; mn.o_sh = out->stride_head;
+    mn.lse = lse; mn.n = P.n_q; mn.h = P.hq; mn.d = P.d;
+    TRY(hip_check(launch_merge_n(mn, s), "segment merge"));
+  }
+  return ok();
+}
+
+attn_status attn_merge_out_lse(const attn_tensor *out, float *lse, const attn_tensor *block_out,
+                               const float *block_lse, const int32_t *cu_seqlens, int32_t num_seqs,
+                               uint32_t q_view, float *block_weight, const attn_tensor *final_out, int32_t init,
+                               void *stream) {
+  TRY(check_tensor(out, "out"));
+  if (out->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "running out must be f32");
+  TRY(check_tensor(block_out, "block_out"));
+  TRY(check_hd(out->head_dim));
+  if (block_out->n_tok != out->n_tok || block_out->n_head != out->n_head || block_out->head_dim != out->head_dim)
+    return fail(ATTN_ERR_SHAPE, "block_out shape differs from out");
+  if (final_out) {
+    TRY(check_tensor(final_out, "final_out"));
+    if (final_out->n_tok != out->n_tok || final_out->n_head != out->n_head || final_out->head_dim != out->head_dim)
+      return fail(ATTN_ERR_SHAPE, "final_out shape differs from out");
+  }
+  if (!lse || !block_lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (q_view > 2) return fail(ATTN_ERR_INVALID, "bad view %u", q_view);
+  if (q_view != 0 && (!cu_seqlens || num_seqs <= 0)) return fail(ATTN_ERR_NULL, "a view needs cu_seqlens");
+  MergeArgs a;
+  a.out = (float *)out->data; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
+  a.lse = lse;
+  a.bout = block_out->data; a.bout_dtype = block_out->dtype; a.b_st = block_out->stride_tok; a.b_sh = block_out->stride_head;
+  a.blse = block_lse; a.weight = block_weight;
+  a.fout = final_out ? final_out->data : nullptr;
+  a.fout_dtype = final_out ? final_out->dtype : ATTN_F32;
+  a.f_st = final_out ? final_out->stride_tok : 0; a.f_sh = final_out ? final_out->stride_head : 0;
+  a.cu = cu_seqlens; a.num_seqs = num_seqs; a.view = (int32_t)q_view;
+  a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim; a.init = init ? 1 : 0;
+  return hip_check(launch_merge(a, (hipStream_t)stream), "merge kernel");
+}
+
+attn_status attn_merge_n(int32_t n_parts, const attn_tensor *parts_out, const float *const *parts_lse,
+                         const attn_tensor *out, float *lse, void *stream) {
+  if (n_parts < 1 || n_parts > 16) return fail(ATTN_ERR_INVALID, "n_parts must be in [1, 16]");
+  if (!parts_out || !parts_lse || !lse) return fail(ATTN_ERR_NULL, "NULL argument");
+  TRY(check_tensor(out, "out"));
+  TRY(check_hd(out->head_dim));
+  MergeNArgs a{};
+  a.n_parts = n_parts;
+  for (int i = 0; i < n_parts; ++i) {
+    TRY(check_tensor(&parts_out[i], "parts_out[i]"));
+    if (parts_out[i].n_tok != out->n_tok || parts_out[i].n_head != out->n_head || parts_out[i].head_dim != out->head_dim)
+      return fail(ATTN_ERR_SHAPE, "parts_out[%d] shape differs from out", i);
+    if (!parts_lse[i]) return fail(ATTN_ERR_NULL, "parts_lse[%d] is NULL", i);
+    a.pout[i] = parts_out[i].data; a.pdtype[i] = parts_out[i].dtype;
+    a.p_st[i] = parts_out[i].stride_tok; a.p_sh[i] = parts_out[i].stride_head;
+    a.plse[i] = parts_lse[i];
+  }
+  a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
+  a.lse = lse; a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim;
+  return hip_check(launch_merge_n(a, (hipStream_t)stream), "merge_n kernel");
+}
+
+attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
+  TRY(check_tensor(dout, "dout"));
+  TRY(check_tensor(out, "out"));
+  TRY(check_hd(out->head_dim));
+  if (dout->n_tok != out->n_tok || dout->n_head != out->n_head || dout->head_dim != out->head_dim)
+    return fail(ATTN_ERR_SHAPE, "dout/out shapes differ");
+  if (!delta) return fail(ATTN_ERR_NULL, "delta is NULL");
+  DeltaArgs a;
+  a.dout = dout->data; a.dtype_do = dout->dtype; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
+  a.out = out->data; a.dtype_o = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
+  a.delta = delta; a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim;
+  return hip_check(launch_delta(a, (hipStream_t)stream), "delta kernel");
+}
+
+attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                           const attn_tensor *out, const float *lse, const float *delta, const int32_t *cu_seqlens_q,
+                           const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           const attn_mask *mask, float scale, const attn_tensor *dq, const attn_tensor *dk,
+                           const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  TRY(check_qkv(q, k, v));
+  TRY(check_mask(mask));
+  if (mask && (mask->block_table || mask->seg_size > 0))
+    return fail(ATTN_ERR_UNSUPPORTED, "paged keys and segments are forward-only");
+  TRY(check_tensor(dout, "dout"));
+  if (dout->dtype != q->dtype) return fail(ATTN_ERR_DTYPE, "dout dtype differs from q");
+  if (dout->n_tok != q->n_tok || dout->n_head != q->n_head || dout->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "dout must be shaped like q");
+  if (!delta) {
+    TRY(check_tensor(out, "out"));
+    if (out->n_tok != q->n_tok || out->n_head != q->n_head || out->head_dim != q->head_dim)
+      return fail(ATTN_ERR_SHAPE, "out must be shaped like q");
+  }
+  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  const attn_tensor *gr[3] = {dq, dk, dv};
+  const char *gn[3] = {"dq", "dk", "dv"};
+  for (int i = 0; i < 3; ++i) {
+    TRY(check_tensor(gr[i], gn[i]));
+    if (gr[i]->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "%s must be f32", gn[i]);
+  }
+  if (dq->n_tok != q->n_tok || dq->n_head != q->n_head || dq->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "dq must be shaped like q");
+  for (int i = 1; i < 3; ++i)
+    if (gr[i]->n_tok != k->n_tok || gr[i]->n_head != k->n_head || gr[i]->head_dim != k->head_dim)
+      return fail(ATTN_ERR_SHAPE, "%s must be shaped like k", gn[i]);
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative sizes");
+  if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
+  const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, delta == nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (num_seqs == 0 || q->n_tok == 0 || k->n_tok == 0) return ok();
+
+  char *w = (char *)workspace;
+  const int64_t capq = sched_capacity(q->n_tok, num_seqs, kBwdTile, 1);
+  const int64_t capk = sched_capacity(k->n_tok, num_seqs, kBwdTile, 1);
+  SchedBufs sq = sched_carve(w, capq);
+  w += align256(sched_bytes(capq));
+  SchedBufs sk = sched_carve(w, capk);
+  w += align256(sched_bytes(capk));
+  if (!delta) {
+    float *dl = (float *)w;
+    TRY(attn_bwd_delta(dout, out, dl, stream));
+    delta = dl;
+  }
+  MaskDev md = mask_dev(mask);
+  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN, 0, 1,
+                                sq, s), "scheduler"));
+  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ, 1, 1,
+                                sk, s), "scheduler"));
+  BwdArgs a;
+  a.q = tdev(q); a.k = tdev(k); a.v = tdev(v); a.dout = tdev(dout);
+  a.dtype = q->dtype; a.head_dim = (int32_t)q->head_dim; a.hq = (int32_t)q->n_head; a.hkv = (int32_t)k->n_head;
+  a.scale = scale; a.mask = md; a.lse = lse; a.delta = delta; a.n_q = q->n_tok; a.n_k = k->n_tok;
+  a.dq = (float *)dq->data; a.dq_st = dq->stride_tok; a.dq_sh = dq->stride_head;
+  a.dk = (float *)dk->data; a.dk_st = dk->stride_tok; a.dk_sh = dk->stride_head;
+  a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;
+  a.qsched = sq; a.ksched = sk; a.q_items = capq; a.k_items = capk;
+  return hip_check(launch_bwd(a, s), "backward kernels");
+}
+
+attn_status attn_zigzag_shard(const attn_tensor *src, const int32_t *cu_seqlens_global, int32_t num_seqs,
+                              int32_t max_seqlen, int32_t cp, int32_t rank, const attn_tensor *dst, void *stream) {
+  TRY(check_tensor(src, "src"));
+  TRY(check_tensor(dst, "dst"));
+  if (cp < 1 || rank < 0 || rank >= cp) return fail(ATTN_ERR_INVALID, "need 0 <= rank < cp");
+  if (src->dtype != dst->dtype || src->n_head != dst->n_head || src->head_dim != dst->head_dim)
+    return fail(ATTN_ERR_SHAPE, "src/dst differ in dtype or head layout");
+  if ((src->head_dim * esize(src->dtype)) % 16) return fail(ATTN_ERR_LAYOUT, "head rows must be 16-byte multiples");
+  if (dst->n_tok * cp != src->n_tok) return fail(ATTN_ERR_SHAPE, "dst must hold n_src / cp rows");
+  if (num_seqs < 0 || max_seqlen < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative sizes");
+  if (num_seqs > 0 && !cu_seqlens_global) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  return hip_check(launch_zigzag_shard(src->data, src->stride_tok, src->stride_head, src->n_tok, dst->data,
+                                       dst->stride_tok, dst->stride_head, dst->n_tok, esize(src->dtype),
+                                       src->n_head, src->head_dim, cu_seqlens_global, num_seqs, max_seqlen, cp,
+                                       rank, (hipStream_t)stream),
+                   "zigzag shard kernel");
+}
+
+// ---------------------------------------------------------------------------
+// virtual-rank schedules
+// ---------------------------------------------------------------------------
+namespace {
+
+attn_mask make_mask(uint32_t causal, uint32_t qv, uint32_t kv) {
+  attn_mask m;
+  memset(&m, 0, sizeof m);
+  m.struct_size = sizeof(attn_mask);
+  m.causal = causal;
+  m.q_view = qv;
+  m.k_view = kv;
+  return m;
+}
+
+// Block kind of rank r at zig-zag step s (src = (r - s) mod cp):
+// s == 0 causal over own rows; src < r: all q rows x src's front halves;
+// src > r: q back halves x all of src's rows (both unmasked).
+attn_mask zigzag_mask(int cp, int r, int s) {
+  (void)cp;
+  if (s == 0) return make_mask(1, ATTN_VIEW_ALL, ATTN_VIEW_ALL);
+  if (s <= r) return make_mask(0, ATTN_VIEW_ALL, ATTN_VIEW_FRONT);
+  return make_mask(0, ATTN_VIEW_BACK, ATTN_VIEW_ALL);
+}
+
+struct RingLayout {
+  size_t bout_off, blse_off, fwd_off, total;
+};
+
+RingLayout ring_layout(const attn_tensor *q, const attn_tensor *k, int32_t num_seqs, int32_t max_local) {
+  Problem P;
+  P.n_q = q->n_tok; P.hq = q->n_head; P.hkv = k->n_head; P.d = q->head_dim; P.nseg = 0; P.decode = false;
+  P.paged = false; P.n_k_logical = k->n_tok;
+  (void)max_local;
+  RingLayout L;
+  L.bout_off = 0;
+  L.blse_off = align256((size_t)q->n_tok * q->n_head * q->head_dim * esize(q->dtype));
+  L.fwd_off = L.blse_off + align256((size_t)q->n_head * q->n_tok * 4);
+  L.total = L.fwd_off + fwd_ws_bytes(P, num_seqs);
+  return L;
+}
+
+typedef attn_mask (*StepMask)(int cp, int r, int s);
+
+attn_mask ring_mask(int cp, int r, int s) {
+  (void)cp; (void)r;
+  return make_mask(s == 0 ? 1 : 0, ATTN_VIEW_ALL, ATTN_VIEW_ALL);
+}
+
+attn_status check_ring_args(int32_t cp, int32_t rank, const attn_tensor *q, const attn_tensor *k_loc,
+                            const attn_tensor *v_loc) {
+  if (cp < 1 || rank < 0 || rank >= cp) return fail(ATTN_ERR_INVALID, "need 0 <= rank < cp");
+  if (!k_loc || !v_loc) return fail(ATTN_ERR_NULL, "k_loc/v_loc is NULL");
+  for (int i = 0; i < cp; ++i) {
+    TRY(check_qkv(q, &k_loc[i], &v_loc[i]));
+    if (k_loc[i].n_tok != q->n_tok) return fail(ATTN_ERR_SHAPE, "every rank's local K/V must have n_loc rows");
+  }
+  return ok();
+}
+
+attn_status run_ring_fwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk, const attn_tensor *q,
+                         const attn_tensor *k_loc, const attn_tensor *v_loc, const int32_t *cu, int32_t num_seqs,
+                         int32_t max_local, float scale, const attn_tensor *out_acc, const attn_tensor *out,
+                         float *lse, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_ring_args(cp, rank, q, k_loc, v_loc));
+  TRY(check_tensor(out_acc, "out_acc"));
+  if (out_acc->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "out_acc must be f32");
+  TRY(check_tensor(out, "out"));
+  RingLayout L = ring_layout(q, &k_loc[0], num_seqs, max_local);
+  if (!ws || ws_bytes < L.total) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", L.total);
+  char *w = (char *)ws;
+  attn_tensor bout = *q;
+  bout.data = w + L.bout_off;
+  bout.stride_head = q->head_dim;
+  bout.stride_tok = q->n_head * q->head_dim;
+  float *blse = (float *)(w + L.blse_off);
+  void *fws = w + L.fwd_off;
+  const size_t fws_bytes = L.total - L.fwd_off;
+  for (int s = 0; s < n_steps; ++s) {
+    const int src = ((rank - s) % cp + cp) % cp;
+    attn_mask m = mk(cp, rank, s);
+    const bool last = s == n_steps - 1;
+    if (s == 0) {
+      // the first block initialises the running state
+      const attn_tensor *dst = (n_steps == 1) ? out : out_acc;
+      TRY(attn_block_fwd(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, dst, lse,
+                         fws, fws_bytes, stream));
+      continue;
+    }
+    TRY(attn_block_fwd(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, &bout, blse,
+                       fws, fws_bytes, stream));
+    TRY(attn_merge_out_lse(out_acc, lse, &bout, blse, cu, num_seqs, m.q_view, nullptr, last ? out : nullptr, 0,
+                           stream));
+  }
+  return ok();
+}
+
+attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk, const attn_tensor *dout,
+                         const attn_tensor *q, const attn_tensor *k_loc, const attn_tensor *v_loc,
+                         const attn_tensor *out, const float *lse, const int32_t *cu, int32_t num_seqs,
+                         int32_t max_local, float scale, const attn_tensor *dq, const attn_tensor *dk_loc,
+                         const attn_tensor *dv_loc, void *ws, size_t ws_bytes, void *stream) {
+  TRY(check_ring_args(cp, rank, q, k_loc, v_loc));
+  if (!dk_loc || !dv_loc) return fail(ATTN_ERR_NULL, "dk_loc/dv_loc is NULL");
+  TRY(check_tensor(out, "out"));
+  const size_t dbytes = align256((size_t)q->n_head * q->n_tok * 4);
+  const size_t bneed = bwd_ws_bytes(q->n_tok, k_loc[0].n_tok, q->n_head, num_seqs, false);
+  if (!ws || ws_bytes < dbytes + bneed) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", dbytes + bneed);
+  float *delta = (float *)ws;
+  TRY(attn_bwd_delta(dout, out, delta, stream));
+  for (int s = 0; s < n_steps; ++s) {
+    const int src = ((rank - s) % cp + cp) % cp;
+    attn_mask m = mk(cp, rank, s);
+    TRY(attn_block_bwd(dout, q, &k_loc[src], &v_loc[src], out, lse, delta, cu, cu, num_seqs, max_local, max_local,
+                       &m, scale, dq, &dk_loc[src], &dv_loc[src], (char *)ws + dbytes, ws_bytes - dbytes, stream));
+  }
+  return ok();
+}
+
+}  // namespace
+
+attn_status attn_zigzag_workspace_size(int32_t cp, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
+                                       int32_t max_seqlen_local, size_t *bytes) {
+  if (!bytes) return fail(ATTN_ERR_NULL, "bytes is NULL");
+  if (cp < 1) return fail(ATTN_ERR_INVALID, "cp must be >= 1");
+  TRY(check_tensor(q, "q"));
+  TRY(check_tensor(k, "k"));
+  const size_t f = ring_layout(q, k, num_seqs, max_seqlen_local).total;
+  const size_t b = align256((size_t)q->n_head * q->n_tok * 4) + bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, false);
+  *bytes = f > b ? f : b;
+  return ok();
+}
+
+attn_status attn_zigzag_fwd(int32_t cp, int32_t rank, const attn_tensor *q, const attn_tensor *k_loc,
+                            const attn_tensor *v_loc, const int32_t *cu_local, int32_t num_seqs,
+                            int32_t max_seqlen_local, float scale, const attn_tensor *out_acc, const attn_tensor *out,
+                            float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  return run_ring_fwd(cp, rank, cp, zigzag_mask, q, k_loc, v_loc, cu_local, num_seqs, max_seqlen_local, scale, out_acc,
+                      out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, const attn_tensor *q,
+                            const attn_tensor *k_loc, const attn_tensor *v_loc, const attn_tensor *out, const float *lse,
+                            const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local, float scale,
+                            const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  return run_ring_bwd(cp, rank, cp, zigzag_mask, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs, max_seqlen_local,
+                      scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_ring_fwd(int32_t cp, int32_t rank, const attn_tensor *q, const attn_tensor *k_loc,
+                          const attn_tensor *v_loc, const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local,
+                          float scale, const attn_tensor *out_acc, const attn_tensor *out, float *lse, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (cp < 1 || rank < 0 || rank >= cp) return fail(ATTN_ERR_INVALID, "need 0 <= rank < cp");
+  return run_ring_fwd(cp, rank, rank + 1, ring_mask, q, k_loc, v_loc, cu_local, num_seqs, max_seqlen_local, scale,
+                      out_acc, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_ring_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, const attn_tensor *q,
+                          const attn_tensor *k_loc, const attn_tensor *v_loc, const attn_tensor *out, const float *lse,
+                          const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local, float scale,
+                          const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  if (cp < 1 || rank < 0 || rank >= cp) return fail(ATTN_ERR_INVALID, "need 0 <= rank < cp");
+  return run_ring_bwd(cp, rank, rank + 1, ring_mask, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs,
+                      max_seqlen_local, scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, size_t *bytes) {
+  if (!bytes) return fail(ATTN_ERR_NULL, "bytes is NULL");
+  if (R < 1 || R > 16) return fail(ATTN_ERR_INVALID, "R must be in [1, 16]");
+  Problem P;
+  TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+  P.decode = false;
+  const size_t part = align256((size_t)P.n_q * P.hq * P.d * 4) + align256((size_t)P.hq * P.n_q * 4);
+  *bytes = (size_t)R * part + fwd_ws_bytes(P, num_seqs);
+  return ok();
+}
+
+attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_caches, const attn_tensor *v_caches,
+                         const int32_t *const *block_tables, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                         int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask,
+                         float scale, const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  if (R < 1 || R > 16) return fail(ATTN_ERR_INVALID, "R must be in [1, 16]");
+  if (!k_caches || !v_caches || !block_tables || !mask) return fail(ATTN_ERR_NULL, "NULL argument");
+  TRY(check_mask(mask));
+  if (mask->kv_interleave != 0 && mask->kv_interleave != R)
+    return fail(ATTN_ERR_INVALID, "kv_interleave must be 0 (contiguous) or R");
+  size_t need = 0;
+  TRY(attn_kvp_workspace_size(R, q, &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, &need));
+  if (!workspace || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
+  TRY(check_tensor(out, "out"));
+  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  char *w = (char *)workspace;
+  const size_t obytes = align256((size_t)q->n_tok * q->n_head * q->head_dim * 4);
+  const size_t lbytes = align256((size_t)q->n_head * q->n_tok * 4);
+  std::vector<attn_tensor> parts(R);
+  std::vector<const float *> plse(R);
+  char *fws = w + (size_t)R * (obytes + lbytes);
+  const size_t fws_bytes = workspace_bytes - (size_t)R * (obytes + lbytes);
+  for (int r = 0; r < R; ++r) {
+    attn_tensor &po = parts[r];
+    po = *q;
+    po.dtype = ATTN_F32;
+    po.data = w + (size_t)r * (obytes + lbytes);
+    po.stride_head = q->head_dim;
+    po.stride_tok = q->n_head * q->head_dim;
+    float *pl = (float *)(w + (size_t)r * (obytes + lbytes) + obytes);
+    plse[r] = pl;
+    attn_mask m = *mask;
+    if (!block_tables[r]) return fail(ATTN_ERR_NULL, "block_tables[%d] is NULL", r);
+    m.block_table = block_tables[r];
+    if (mask->kv_interleave == R) m.kv_rank = r;
+    else m.k_pos_offset = mask->k_pos_offset + (int64_t)r * max_seqlen_k;
+    TRY(attn_block_fwd(q, &k_caches[r], &v_caches[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k,
+                       &m, scale, &po, pl, fws, fws_bytes, stream));
+  }
+  return attn_merge_n(R, parts.data(), plse.data(), out, lse, stream);
+}
+
+// ---------------------------------------------------------------------------
+// device-content validation (synchronises)
+// ---------------------------------------------------------------------------
+attn_status attn_validate_inputs(const attn_tensor *q, const attn_tensor *k, const int32_t *cu_seqlens_q,
+                                 const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, const attn_mask *mask, int32_t zigzag_cp, int32_t one_query,
+                                 void *stream) {
+  TRY(check_tensor(q, "q"));
+  TRY(check_tensor(k, "k"));
+  TRY(check_mask(mask));
+  if (num_seqs < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs");
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> cq(num_seqs + 1), ck(num_seqs + 1);
+  TRY(hip_check(hipMemcpyAsync(cq.data(), cu_seqlens_q, cq.size() * 4, hipMemcpyDeviceToHost, s), "copy"));
+  TRY(hip_check(hipMemcpyAsync(ck.data(), cu_seqlens_k, ck.size() * 4, hipMemcpyDeviceToHost, s), "copy"));
+  std::vector<int32_t> bt;
+  const bool paged = mask && mask->block_table;
+  if (paged) {
+    bt.resize(mask->max_blocks);
+    TRY(hip_check(hipMemcpyAsync(bt.data(), mask->block_table, bt.size() * 4, hipMemcpyDeviceToHost, s), "copy"));
+  }
+  TRY(hip_check(hipStreamSynchronize(s), "sync"));
+  const int64_t nk = paged ? (int64_t)mask->max_blocks * mask->block_size : k->n_tok;
+  if (cq[0] != 0 || ck[0] != 0) return fail(ATTN_ERR_CONTENT, "cu_seqlens must start at 0");
+  for (int d = 0; d < num_seqs; ++d) {
+    const int64_t lq = (int64_t)cq[d + 1] - cq[d], lk = (int64_t)ck[d + 1] - ck[d];
+    if (lq < 0 || lk < 0) return fail(ATTN_ERR_CONTENT, "cu_seqlens decreases at document %d", d);
+    if (lq > max_seqlen_q || lk > max_seqlen_k)
+      return fail(ATTN_ERR_CONTENT, "document %d longer than max_seqlen (%lld/%lld)", d, (long long)lq, (long long)lk);
+    if (zigzag_cp > 0 && lq % (2 * zigzag_cp))
+      return fail(ATTN_ERR_CONTENT, "document %d length %lld not a multiple of 2*cp", d, (long long)lq);
+    if (one_query && lq != 1) return fail(ATTN_ERR_CONTENT, "document %d has %lld queries (decode needs 1)", d, (long long)lq);
+  }
+  if (cq[num_seqs] > q->n_tok || ck[num_seqs] > nk) return fail(ATTN_ERR_CONTENT, "cu_seqlens exceed the tensors");
+  if (paged) {
+    const int64_t pages = k->n_tok / mask->block_size;
+    const int64_t used = (ck[num_seqs] + mask->block_size - 1) / mask->block_size;
+    for (int64_t b = 0; b < used && b < (int64_t)bt.size(); ++b)
+      if (bt[b] < 0 || bt[b] >= pages) return fail(ATTN_ERR_CONTENT, "block_table[%lld] = %d out of range", (long long)b, bt[b]);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,369 @@
+// Block backward with the merged (out, lse) (gfx950).
+//
+// NeMo AutoModel zigzag_ring_attention, `zigzag_ring_flash_attn_varlen_backward`:
+// every block's backward receives the FINAL merged out and lse, so with
+//     P  = exp(scale q.k - lse),   dP = dout . v,   dS = P (dP - delta),
+//     delta = <dout, out>  (merged out, computed once by attn_bwd_delta)
+// the block's share of the joint-softmax gradient is
+//     dq += scale dS k,   dk += scale dS^T q,   dv += P^T dout.
+//
+// Two kernels, no floating-point atomics (deterministic):
+//   * dK/dV: a workgroup owns 128 keys of one kv head (wave w: keys 32w..),
+//     keeps K and V of its keys in registers and loops over the q heads of the
+//     kv group and the 64-row query tiles that can see its keys. Scores are
+//     computed as S = Q K^T with the 32x32 MFMA, so a lane owns one key
+//     (column) and 16 query rows; P and dS are then already the B operand of
+//     dV^T += dO^T P and dK^T += Q^T dS, whose A operands are read from the
+//     query / dout tiles in LDS with the transpose read.
+//   * dQ: a workgroup owns 128 query rows of one q head (like the forward),
+//     keeps Q and dO in registers, stages K/V tiles, computes S^T = K Q^T and
+//     dP^T = V dO^T, and accumulates dQ^T += K^T dS^T (K^T by transpose read).
+#include "internal.h"
+
+namespace attn {
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS pitch (elements) of tiles read both row-wise (16-byte reads of 16 rows)
+// and with the 4-row transpose read: bf16 D + 40 keeps the row reads conflict
+// free and the transpose reads at most 2-way; f32 tiles use an odd pitch.
+template <typename T, int D> struct Pitch;
+template <int D> struct Pitch<bf16, D> { static constexpr int both = D + 40, rows = D + 8; };
+template <int D> struct Pitch<float, D> { static constexpr int both = D + 1, rows = D + 1; };
+
+struct BwdParams {
+  const void *q, *k, *v, *dout;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, do_st, do_sh;
+  int32_t hq, group;
+  float scale, scale_log2;
+  MaskDev m;
+  const float *lse, *delta;
+  int64_t n_q;
+  float *dq; int64_t dq_st, dq_sh;
+  float *dk; int64_t dk_st, dk_sh;
+  float *dv; int64_t dv_st, dv_sh;
+  const WorkItem *items; const int32_t *order; const int32_t *count;
+};
+
+// Row-operand fragment of a 32x32 MFMA from a tile in LDS: lane row `r`, k-step s.
+template <typename T>
+__device__ __forceinline__ typename Mfma32<T>::Frag lds_row_frag(const T *base, int pitch, int r, int s, int g) {
+  constexpr int KV = Mfma32<T>::KV;
+  if constexpr (sizeof(T) == 2) return *reinterpret_cast<const bf16x8 *>(base + r * pitch + s * 2 * KV + g * KV);
+  else return base[r * pitch + s * 2 + g];
+}
+
+// Row-operand fragment straight from global memory (zero when !ok).
+template <typename T>
+__device__ __forceinline__ typename Mfma32<T>::Frag glob_row_frag(const T *row, int s, int g, bool ok) {
+  constexpr int KV = Mfma32<T>::KV;
+  if constexpr (sizeof(T) == 2) {
+    i32x4 v = ok ? ld16(row + s * 2 * KV + g * KV) : i32x4{0, 0, 0, 0};
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    return ok ? row[s * 2 + g] : 0.f;
+  }
+}
+
+// acc += X^T(d rows dt*32.., k = 32 tile rows starting at r0) * B, where B is
+// held in C layout (register j <-> tile row c_row(j)) in `pv` (16 values).
+template <typename T>
+__device__ __forceinline__ f32x16 acc_transposed(f32x16 acc, const T *base, int pitch, int r0, int dt,
+                                                 const float (&pv)[16], int lane) {
+  const int g = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    const int u = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = (bf16)pv[t * 8 + e];
+      const int ra = r0 + t * 16 + 4 * g + (u >> 2);
+      const int col = dt * 32 + dh * 16 + 4 * (u & 3);
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + ra * pitch + col));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (ra + 8) * pitch + col));
+      bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+      bf16x8 a;
+      a[0] = l4[0]; a[1] = l4[1]; a[2] = l4[2]; a[3] = l4[3];
+      a[4] = h4[0]; a[5] = h4[1]; a[6] = h4[2]; a[7] = h4[3];
+      acc = Mfma32<bf16>::mma(a, b, acc);
+    }
+  } else {
+    const int l32 = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      acc = Mfma32<float>::mma(base[(r0 + c_row(j, lane)) * pitch + dt * 32 + l32], pv[j], acc);
+  }
+  return acc;
+}
+
+// Stage rows [r0, r0 + nrows) (< lim valid) of a [tok, head, D] tensor into LDS.
+template <typename T, int D, int NROWS>
+__device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src, int64_t st, int64_t sh, int head,
+                                           int64_t r0, int64_t lim, int tid) {
+  constexpr int CH = 16 / sizeof(T);
+  constexpr int NCH = NROWS * D / CH / 256;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int ci = tid + 256 * c;
+    const int r = ci / (D / CH);
+    const int col = (ci % (D / CH)) * CH;
+    const int64_t row = r0 + r;
+    i32x4 v = row < lim ? ld16(src + row * st + (int64_t)head * sh + col) : i32x4{0, 0, 0, 0};
+    if constexpr (sizeof(T) == 2) {
+      st16(dst + r * pitch + col, v);
+    } else {
+      float4 f = __builtin_bit_cast(float4, v);
+      dst[r * pitch + col] = f.x; dst[r * pitch + col + 1] = f.y;
+      dst[r * pitch + col + 2] = f.z; dst[r * pitch + col + 3] = f.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
+  using M = Mfma32<T>;
+  constexpr int NS = D / (2 * M::KV);
+  constexpr int ND = D / 32;
+  constexpr int QB = kBwdBQ;  // query rows per staged tile
+  constexpr int PB = Pitch<T, D>::both;
+  __shared__ __attribute__((aligned(16))) T sQ[QB * PB];
+  __shared__ __attribute__((aligned(16))) T sO[QB * PB];
+  __shared__ float sL[QB], sDl[QB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int hkv_count = p.hq / p.group;
+  const int rank = blockIdx.x / hkv_count;
+  const int hk = blockIdx.x - rank * hkv_count;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const MaskDev &m = p.m;
+
+  const int64_t kr0 = it.k0 + 32 * w;          // first key of this wave
+  const int64_t key = kr0 + l32;
+  const bool key_ok = key < it.k1;
+  const bool wave_on = kr0 < it.k1;
+  const int64_t kp_lane = m.pm.kpos(key - it.kdoc0);
+  const int64_t wk_lo = m.pm.kpos(kr0 - it.kdoc0);
+  const int64_t wk_hi = m.pm.kpos((kr0 + 31 < it.k1 ? kr0 + 31 : it.k1 - 1) - it.kdoc0);
+
+  typename M::Frag kf[NS], vf[NS];
+  {
+    const T *krow = (const T *)p.k + key * p.k_st + (int64_t)hk * p.k_sh;
+    const T *vrow = (const T *)p.v + key * p.v_st + (int64_t)hk * p.v_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = glob_row_frag<T>(krow, s, g, key_ok);
+      vf[s] = glob_row_frag<T>(vrow, s, g, key_ok);
+    }
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+
+  for (int hh = 0; hh < p.group; ++hh) {
+    const int h = hk * p.group + hh;
+    for (int64_t qt = it.q0; qt < it.q1; qt += QB) {
+      __syncthreads();
+      stage_rows<T, D, QB>(sQ, PB, (const T *)p.q, p.q_st, p.q_sh, h, qt, it.q1, tid);
+      stage_rows<T, D, QB>(sO, PB, (const T *)p.dout, p.do_st, p.do_sh, h, qt, it.q1, tid);
+      if (tid < QB) {
+        const int64_t row = qt + tid;
+        const bool ok = row < it.q1;
+        const float l = ok ? p.lse[(int64_t)h * p.n_q + row] : neg_inf();
+        // rows without a finite lse (none visible, or padding) contribute nothing
+        sL[tid] = (l == neg_inf()) ? __builtin_inff() : l * kLog2e;
+        sDl[tid] = ok ? p.delta[(int64_t)h * p.n_q + row] : 0.f;
+      }
+      __syncthreads();
+      if (!wave_on) continue;
+#pragma unroll
+      for (int sub = 0; sub < QB / 32; ++sub) {
+        const int64_t qs0 = qt + sub * 32;
+        if (qs0 >= it.q1) break;
+        const int64_t qlast = (qs0 + 31 < it.q1 ? qs0 + 31 : it.q1 - 1);
+        const int64_t qp_lo = m.q_pos_offset + (qs0 - it.qdoc0);
+        const int64_t qp_hi = m.q_pos_offset + (qlast - it.qdoc0);
+        if (m.causal && wk_lo > qp_hi) continue;
+        if (m.window > 0 && wk_hi <= qp_lo - m.window) continue;
+        const bool full = (!m.causal || wk_hi <= qp_lo) && (m.window <= 0 || wk_lo > qp_hi - m.window);
+        // S = Q K^T and dP = dO V^T: lane column = its key, rows = 16 query rows
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          s = M::mma(lds_row_frag<T>(sQ, PB, sub * 32 + l32, st, g), kf[st], s);
+          dp = M::mma(lds_row_frag<T>(sO, PB, sub * 32 + l32, st, g), vf[st], dp);
+        }
+        float pv[16], ds[16];
+        const int64_t qp0 = m.q_pos_offset + (qt - it.qdoc0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int qi = sub * 32 + c_row(j, lane);
+          const bool vis = full | visible(qp0 + qi, kp_lane, m.causal, m.window);
+          const float e = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -sL[qi]));
+          pv[j] = vis ? e : 0.f;
+          ds[j] = pv[j] * (dp[j] - sDl[qi]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          dv[dt] = acc_transposed<T>(dv[dt], sO, PB, sub * 32, dt, pv, lane);
+          dk[dt] = acc_transposed<T>(dk[dt], sQ, PB, sub * 32, dt, ds, lane);
+        }
+      }
+    }
+  }
+  if (!key_ok) return;
+  // dK^T / dV^T in C layout: lane column = its key, rows d = dt*32 + c_row(j)
+  float *dkr = p.dk + key * p.dk_st + (int64_t)hk * p.dk_sh;
+  float *dvr = p.dv + key * p.dv_st + (int64_t)hk * p.dv_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      float4 a = *reinterpret_cast<float4 *>(dkr + d0);
+      a.x += p.scale * dk[dt][4 * j4]; a.y += p.scale * dk[dt][4 * j4 + 1];
+      a.z += p.scale * dk[dt][4 * j4 + 2]; a.w += p.scale * dk[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dkr + d0) = a;
+      float4 b = *reinterpret_cast<float4 *>(dvr + d0);
+      b.x += dv[dt][4 * j4]; b.y += dv[dt][4 * j4 + 1]; b.z += dv[dt][4 * j4 + 2]; b.w += dv[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dvr + d0) = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
+  using M = Mfma32<T>;
+  constexpr int NS = D / (2 * M::KV);
+  constexpr int ND = D / 32;
+  constexpr int KB = kFwdBN;  // keys per staged tile
+  constexpr int PK = Pitch<T, D>::both;
+  constexpr int PV = Pitch<T, D>::rows;
+  __shared__ __attribute__((aligned(16))) T sK[KB * PK];
+  __shared__ __attribute__((aligned(16))) T sV[KB * PV];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int rank = blockIdx.x / p.hq;
+  const int h = blockIdx.x - rank * p.hq;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const int hk = h / p.group;
+  const MaskDev &m = p.m;
+
+  const int64_t r0 = it.q0 + 32 * w;
+  const int64_t row = r0 + l32;
+  const bool row_ok = row < it.q1;
+  const bool wave_on = r0 < it.q1;
+  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
+  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
+  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+
+  typename M::Frag qf[NS], of[NS];
+  {
+    const T *qrow = (const T *)p.q + row * p.q_st + (int64_t)h * p.q_sh;
+    const T *orow = (const T *)p.dout + row * p.do_st + (int64_t)h * p.do_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = glob_row_frag<T>(qrow, s, g, row_ok);
+      of[s] = glob_row_frag<T>(orow, s, g, row_ok);
+    }
+  }
+  float lrow = row_ok ? p.lse[(int64_t)h * p.n_q + row] : neg_inf();
+  lrow = lrow == neg_inf() ? __builtin_inff() : lrow * kLog2e;
+  const float drow = row_ok ? p.delta[(int64_t)h * p.n_q + row] : 0.f;
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) dq[i] = f32x16{};
+
+  for (int64_t kt = it.k0; kt < it.k1; kt += KB) {
+    __syncthreads();
+    stage_rows<T, D, KB>(sK, PK, (const T *)p.k, p.k_st, p.k_sh, hk, kt, it.k1, tid);
+    stage_rows<T, D, KB>(sV, PV, (const T *)p.v, p.v_st, p.v_sh, hk, kt, it.k1, tid);
+    __syncthreads();
+    if (!wave_on) continue;
+    const int64_t klast = (kt + KB <= it.k1 ? kt + KB : it.k1) - 1;
+    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
+    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
+    if (m.causal && kp_lo > wq_hi) continue;
+    if (m.window > 0 && kp_hi <= wq_lo - m.window) continue;
+    const bool full = (kt + KB <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
+                      (m.window <= 0 || kp_lo > wq_hi - m.window);
+#pragma unroll
+    for (int sb = 0; sb < KB / 32; ++sb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(lds_row_frag<T>(sK, PK, sb * 32 + l32, st, g), qf[st], s);
+        dp = M::mma(lds_row_frag<T>(sV, PV, sb * 32 + l32, st, g), of[st], dp);
+      }
+      float ds[16];
+      const int32_t t0 = (int32_t)(kt - it.kdoc0);
+      const int32_t nvalid = (int32_t)(it.k1 - kt);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int32_t kk = sb * 32 + c_row(j, lane);
+        const bool vis = full | ((kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window));
+        const float e = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -lrow));
+        ds[j] = vis ? e * (dp[j] - drow) : 0.f;
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<T>(dq[dt], sK, PK, sb * 32, dt, ds, lane);
+    }
+  }
+  if (!row_ok) return;
+  float *dqr = p.dq + row * p.dq_st + (int64_t)h * p.dq_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      float4 a = *reinterpret_cast<float4 *>(dqr + d0);
+      a.x += p.scale * dq[dt][4 * j4]; a.y += p.scale * dq[dt][4 * j4 + 1];
+      a.z += p.scale * dq[dt][4 * j4 + 2]; a.w += p.scale * dq[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dqr + d0) = a;
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, hipStream_t s) {
+  BwdParams pk = base;
+  pk.items = a.ksched.items; pk.order = a.ksched.order; pk.count = a.ksched.count;
+  const int64_t gk = a.k_items * a.hkv;
+  if (gk > 0) hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  BwdParams pq = base;
+  pq.items = a.qsched.items; pq.order = a.qsched.order; pq.count = a.qsched.count;
+  const int64_t gq = a.q_items * a.hq;
+  if (gq > 0) hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
+  BwdParams p;
+  p.q = a.q.data; p.k = a.k.data; p.v = a.v.data; p.dout = a.dout.data;
+  p.q_st = a.q.st; p.q_sh = a.q.sh; p.k_st = a.k.st; p.k_sh = a.k.sh;
+  p.v_st = a.v.st; p.v_sh = a.v.sh; p.do_st = a.dout.st; p.do_sh = a.dout.sh;
+  p.hq = a.hq; p.group = a.hq / a.hkv;
+  p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
+  p.m = a.mask;
+  p.lse = a.lse; p.delta = a.delta; p.n_q = a.n_q;
+  p.dq = a.dq; p.dq_st = a.dq_st; p.dq_sh = a.dq_sh;
+  p.dk = a.dk; p.dk_st = a.dk_st; p.dk_sh = a.dk_sh;
+  p.dv = a.dv; p.dv_st = a.dv_st; p.dv_sh = a.dv_sh;
+  if (a.dtype == 0) {
+    if (a.head_dim == 128) return launch_bwd_t<bf16, 128>(p, a, s);
+    return launch_bwd_t<bf16, 64>(p, a, s);
+  }
+  if (a.head_dim == 128) return launch_bwd_t<float, 128>(p, a, s);
+  return launch_bwd_t<float, 64>(p, a, s);
+}
+
+}  // namespace attn

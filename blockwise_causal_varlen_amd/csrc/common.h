@@ -1,0 +1,117 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, lane-layout helpers and the key-position map.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// 32x32 MFMA with f32 accumulation. Lane l supplies row (l % 32) of A and
+// column (l % 32) of B; the lane group l / 32 supplies its own KV consecutive
+// k-slots. The result C[m][n] is held by lane n + 32 * ((m / 4) % 2) in
+// register (m / 8) * 4 + m % 4. (Checked on gfx950 against a CPU product.)
+// ---------------------------------------------------------------------------
+template <typename T> struct Mfma32;
+
+template <> struct Mfma32<bf16> {
+  static constexpr int KV = 8;  // elements per lane per instruction (k = 16)
+  typedef bf16x8 Frag;
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma32<float> {
+  static constexpr int KV = 1;  // k = 2
+  typedef float Frag;
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Key (row) index within a 32x32 result tile held in register j of lane l.
+__device__ __forceinline__ int c_row(int j, int lane) {
+  return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+}
+
+// ---------------------------------------------------------------------------
+// conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Cross-lane exchange with lane l ^ 32 (the other half of a 32x32 tile column).
+__device__ __forceinline__ float xor32(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ i32x4 ld16(const void *p) { return *reinterpret_cast<const i32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, i32x4 v) { *reinterpret_cast<i32x4 *>(p) = v; }
+
+// ---------------------------------------------------------------------------
+// Key position map (the visibility rule of the C ABI):
+//   kpos = k_pos_offset + t                                   (contiguous)
+//   kpos = k_pos_offset + ((t / B) * R + r) * B + t % B       (round robin)
+// t is the index of the key inside its document's key buffer. The map is
+// strictly increasing in t, which the tile bounds rely on.
+// ---------------------------------------------------------------------------
+struct PosMap {
+  int64_t k_pos_offset;
+  int32_t interleave;  // R (0 = contiguous)
+  int32_t rank;
+  int32_t block;       // B
+  __device__ __forceinline__ int64_t kpos(int64_t t) const {
+    if (interleave == 0) return k_pos_offset + t;
+    int64_t b = t / block, o = t - b * block;
+    return k_pos_offset + (b * interleave + rank) * block + o;
+  }
+  // Branch-free 32-bit form for per-element masks (t, positions < 2^31 within
+  // one document's window of interest; the offset is applied in 64 bits).
+  __device__ __forceinline__ int64_t kpos32(int32_t t) const {
+    const int32_t bs = interleave ? block : 1;  // no division by zero when contiguous
+    const int32_t b = t / bs;
+    const int32_t rr = interleave ? ((b * interleave + rank) * bs + (t - b * bs)) : t;
+    return k_pos_offset + rr;
+  }
+  // Number of keys t in [0, n) with kpos(t) <= p (monotone inverse).
+  __device__ __forceinline__ int64_t count_le(int64_t p, int64_t n) const {
+    int64_t lo = 0, hi = n;  // answer in [lo, hi]
+    while (lo < hi) {
+      int64_t mid = (lo + hi) >> 1;
+      if (kpos(mid) <= p) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  }
+};
+
+// Visibility of (query position qp, key position kp) under causal / window,
+// written with bitwise ops so it compiles to selects, not branches.
+__device__ __forceinline__ bool visible(int64_t qp, int64_t kp, int32_t causal, int64_t window) {
+  const bool c = (causal == 0) | (kp <= qp);
+  const bool w = (window <= 0) | (kp > qp - window);
+  return c & w;
+}
+
+}  // namespace attn

@@ -1,0 +1,514 @@
+// Tile scheduler and block-forward kernel (gfx950).
+//
+// Block forward of one attention block over packed varlen documents, as the
+// flash varlen forward the pages call per ring step (NeMo AutoModel
+// zigzag_ring_attention, `_block_forward`; ring_attention, `_fa_forward`):
+// returns the block's normalised output and its log-sum-exp of scaled scores.
+// Masks: causal and sliding window on explicit positions, per-document
+// front/back half views, a round-robin key position map and paged keys (AWS
+// NKI "Attention KV-Parallel Segmented CTE": block_tables, kvp_group_size,
+// sliding_window, seg_size).
+//
+// Kernel shape. A workgroup = 4 waves = 128 query rows of one q head; wave w
+// owns rows [32w, 32w+32). Scores are computed transposed, S^T = K Q^T, with
+// the 32x32 MFMA so that a lane owns one query row (lane % 32) and 16 keys of
+// every 32-key sub-tile: the row max needs one exchange with lane ^ 32, the
+// exponentiated scores are already in the register layout of the B operand of
+// O^T += V^T P^T, and the output rescale is a per-lane scalar. K and V tiles of
+// 64 keys are staged through LDS; V^T operands are read with the gfx950 LDS
+// transpose read (ds_read_b64_tr_b16), K with 16-byte reads on a padded pitch.
+#include "internal.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// Scheduler: one workgroup builds the work list (one item per (q tile,
+// segment)), then orders it by decreasing cost (counting sort on the number of
+// visible key tiles) so that long tiles start first.
+// ---------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+constexpr int kCostBins = 2048;
+
+size_t sched_bytes(int64_t capacity) {
+  size_t b = (size_t)capacity * sizeof(WorkItem);
+  b = (b + 255) & ~(size_t)255;
+  b += ((size_t)capacity * sizeof(int32_t) + 255) & ~(size_t)255;
+  b += 256;
+  return b;
+}
+
+SchedBufs sched_carve(void *ws, int64_t capacity) {
+  char *p = (char *)ws;
+  SchedBufs sb;
+  sb.items = (WorkItem *)p;
+  p += ((size_t)capacity * sizeof(WorkItem) + 255) & ~(size_t)255;
+  sb.order = (int32_t *)p;
+  p += ((size_t)capacity * sizeof(int32_t) + 255) & ~(size_t)255;
+  sb.count = (int32_t *)p;
+  sb.capacity = (int32_t)capacity;
+  return sb;
+}
+
+int64_t sched_capacity(int64_t n_rows, int32_t num_seqs, int32_t tile, int64_t n_seg) {
+  return (n_rows / tile + num_seqs + 1) * (n_seg > 0 ? n_seg : 1);
+}
+
+struct SchedParams {
+  const int32_t *cu_q, *cu_k;
+  int32_t num_seqs;
+  int64_t n_q, n_k;
+  MaskDev m;
+  int32_t tile, key_tile;
+  int32_t by_keys;  // 0: tiles of query rows; 1: tiles of key rows (dK/dV)
+  int32_t max_seg;  // segments the partial buffers hold (longer documents are cut)
+  SchedBufs sb;
+};
+
+__device__ __forceinline__ void view_range(int64_t s, int64_t e, int view, int64_t &a, int64_t &b) {
+  int64_t h = (e - s) / 2;
+  a = s; b = e;
+  if (view == 1) b = s + h;
+  else if (view == 2) a = s + h;
+}
+
+__device__ __forceinline__ int64_t clampi(int64_t x, int64_t lo, int64_t hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
+  __shared__ int32_t s_scan[kSchedThreads];
+  __shared__ int32_t s_hist[kCostBins];
+  __shared__ int32_t s_total;
+  const int tid = threadIdx.x;
+  const MaskDev &m = p.m;
+  int64_t running = 0;
+  for (int c0 = 0; c0 < p.num_seqs; c0 += kSchedThreads) {
+    const int d = c0 + tid;
+    int64_t qs = 0, qe = 0, ks = 0, ke = 0, qa = 0, qb = 0, ka = 0, kb = 0, nseg = 1, ntile = 0;
+    if (d < p.num_seqs) {
+      qs = clampi(p.cu_q[d], 0, p.n_q);
+      qe = clampi(p.cu_q[d + 1], qs, p.n_q);
+      ks = clampi(p.cu_k[d], 0, p.n_k);
+      ke = clampi(p.cu_k[d + 1], ks, p.n_k);
+      view_range(qs, qe, m.q_view, qa, qb);
+      view_range(ks, ke, m.k_view, ka, kb);
+      ntile = p.by_keys ? (kb - ka + p.tile - 1) / p.tile : (qb - qa + p.tile - 1) / p.tile;
+      if (m.seg_size > 0 && !p.by_keys) nseg = (ke - ks + m.seg_size - 1) / m.seg_size;
+      if (nseg > p.max_seg) nseg = p.max_seg;
+      if (nseg < 1) nseg = 1;
+    }
+    int32_t mine = (int32_t)(ntile * nseg);
+    // block exclusive scan
+    s_scan[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
+      int32_t v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int64_t base = running + s_scan[tid] - mine;
+    if (tid == kSchedThreads - 1) s_total = s_scan[tid];
+    __syncthreads();
+    running += s_total;
+    __syncthreads();
+    if (d < p.num_seqs) {
+      const int64_t nk_doc = ke - ks;
+      for (int64_t t = 0; p.by_keys && t < ntile; ++t) {
+        // a tile of keys and the query rows that can see any of them
+        const int64_t k0 = ka + t * p.tile;
+        const int64_t k1 = k0 + p.tile < kb ? k0 + p.tile : kb;
+        int64_t lo = qa, hi = qb;
+        if (m.causal) {  // qpos >= kpos(first key)
+          const int64_t c = qs + (m.pm.kpos(k0 - ks) - m.q_pos_offset);
+          if (c > lo) lo = c;
+        }
+        if (m.window > 0) {  // qpos < kpos(last key) + window
+          const int64_t c = qs + (m.pm.kpos(k1 - 1 - ks) + m.window - m.q_pos_offset);
+          if (c < hi) hi = c;
+        }
+        if (hi < lo) hi = lo;
+        const int64_t idx = base + t;
+        if (idx >= p.sb.capacity) continue;
+        WorkItem it;
+        it.q0 = (int32_t)lo; it.q1 = (int32_t)hi;
+        it.k0 = (int32_t)k0; it.k1 = (int32_t)k1;
+        it.qdoc0 = (int32_t)qs; it.kdoc0 = (int32_t)ks;
+        it.seg = 0;
+        it.cost = (int32_t)((hi - lo + p.key_tile - 1) / p.key_tile + 1);
+        p.sb.items[idx] = it;
+      }
+      for (int64_t t = 0; !p.by_keys && t < ntile; ++t) {
+        const int64_t q0 = qa + t * p.tile;
+        const int64_t q1 = q0 + p.tile < qb ? q0 + p.tile : qb;
+        // keys any row of the tile can see
+        int64_t lo = ka, hi = kb;
+        if (m.causal) {
+          const int64_t pmax = m.q_pos_offset + (q1 - 1 - qs);
+          const int64_t c = ks + m.pm.count_le(pmax, nk_doc);
+          if (c < hi) hi = c;
+        }
+        if (m.window > 0) {
+          const int64_t pmin = m.q_pos_offset + (q0 - qs);
+          const int64_t c = ks + m.pm.count_le(pmin - m.window, nk_doc);
+          if (c > lo) lo = c;
+        }
+        for (int64_t sg = 0; sg < nseg; ++sg) {
+          const int64_t idx = base + t * nseg + sg;
+          if (idx >= p.sb.capacity) continue;
+          int64_t a = lo, b = hi;
+          if (m.seg_size > 0) {
+            const int64_t sa = ks + sg * m.seg_size, sbd = sa + m.seg_size;
+            if (sa > a) a = sa;
+            if (sbd < b) b = sbd;
+          }
+          if (b < a) b = a;
+          WorkItem it;
+          it.q0 = (int32_t)q0; it.q1 = (int32_t)q1;
+          it.k0 = (int32_t)a; it.k1 = (int32_t)b;
+          it.qdoc0 = (int32_t)qs; it.kdoc0 = (int32_t)ks;
+          it.seg = (int32_t)sg;
+          it.cost = (int32_t)((b - a + p.key_tile - 1) / p.key_tile + 1);
+          p.sb.items[idx] = it;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  const int32_t count = (int32_t)(running < p.sb.capacity ? running : p.sb.capacity);
+  // counting sort by decreasing cost
+  for (int i = tid; i < kCostBins; i += kSchedThreads) s_hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < count; i += kSchedThreads) {
+    int c = p.sb.items[i].cost;
+    c = c >= kCostBins ? kCostBins - 1 : c;
+    atomicAdd(&s_hist[kCostBins - 1 - c], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive scan over bins (2048 entries, once per launch)
+    int32_t acc = 0;
+    for (int i = 0; i < kCostBins; ++i) {
+      int32_t v = s_hist[i];
+      s_hist[i] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < count; i += kSchedThreads) {
+    int c = p.sb.items[i].cost;
+    c = c >= kCostBins ? kCostBins - 1 : c;
+    int pos = atomicAdd(&s_hist[kCostBins - 1 - c], 1);
+    p.sb.order[pos] = i;
+  }
+  if (tid == 0) *p.sb.count = count;
+}
+
+hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs, int64_t n_q,
+                           int64_t n_k, const MaskDev &m, int32_t tile, int32_t key_tile,
+                           int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s) {
+  SchedParams p{cu_q, cu_k, num_seqs, n_q, n_k, m, tile, key_tile, by_keys, max_seg < 1 ? 1 : max_seg, sb};
+  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Forward kernel
+// ---------------------------------------------------------------------------
+struct FwdParams {
+  const void *q, *k, *v;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+  int32_t hq, group;
+  float scale_log2;
+  MaskDev m;
+  const int32_t *block_table;
+  int32_t block_size, max_blocks;
+  int64_t page_stride, n_pages;
+  void *out; int64_t o_st, o_sh;
+  float *lse; int64_t lse_n;
+  int32_t segmented;
+  float *part_out, *part_lse;
+  int64_t n_q;
+  const WorkItem *items; const int32_t *order; const int32_t *count;
+};
+
+template <typename T> struct Tile;  // LDS pitches (elements)
+template <> struct Tile<bf16> {
+  template <int D> static constexpr int kpitch() { return D + 8; }   // 16-row b128 reads conflict free
+  template <int D> static constexpr int vpitch() { return D + 32; }  // 4-row transpose reads conflict free
+};
+template <> struct Tile<float> {
+  template <int D> static constexpr int kpitch() { return D + 1; }
+  template <int D> static constexpr int vpitch() { return D + 4; }
+};
+
+// Address of logical key row j (head hk) of a K or V tensor; nullptr when the
+// row has no valid page.
+template <typename T>
+__device__ __forceinline__ const T *key_row(const FwdParams &p, const T *base, int64_t st, int64_t sh,
+                                            int64_t j, int hk) {
+  if (p.block_table == nullptr) return base + j * st + hk * sh;
+  const int64_t b = j / p.block_size;
+  if (b >= p.max_blocks) return nullptr;
+  const int64_t pg = p.block_table[b];
+  if (pg < 0 || pg >= p.n_pages) return nullptr;
+  return base + pg * p.page_stride + hk * sh + (j - b * p.block_size) * st;
+}
+
+template <typename T, int D, typename OutT>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+  using M = Mfma32<T>;
+  constexpr int KV = M::KV;
+  constexpr int KSTEP = 2 * KV;
+  constexpr int NS = D / KSTEP;
+  constexpr int KP = Tile<T>::template kpitch<D>();
+  constexpr int VP = Tile<T>::template vpitch<D>();
+  constexpr int CH = 16 / sizeof(T);                 // elements per 16-byte chunk
+  constexpr int NCH = kFwdBN * D / CH / 256;          // chunks per thread per tensor
+  constexpr int ND = D / 32;
+  constexpr bool kBf16 = sizeof(T) == 2;
+
+  __shared__ __attribute__((aligned(16))) T sK[kFwdBN * KP];
+  __shared__ __attribute__((aligned(16))) T sV[kFwdBN * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int rank = blockIdx.x / p.hq;
+  const int h = blockIdx.x - rank * p.hq;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const int hk = h / p.group;
+  const MaskDev &m = p.m;
+
+  const int64_t r0 = it.q0 + 32 * w;
+  const int64_t row = r0 + l32;
+  const bool row_ok = row < it.q1;
+  const bool wave_on = r0 < it.q1;
+  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
+  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
+  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds row `row`, k-slots of group g.
+  typename M::Frag qf[NS];
+  {
+    const T *qrow = (const T *)p.q + row * p.q_st + h * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (kBf16) {
+        i32x4 v = row_ok ? ld16(qrow + s * KSTEP + g * KV) : i32x4{0, 0, 0, 0};
+        qf[s] = __builtin_bit_cast(bf16x8, v);
+      } else {
+        qf[s] = row_ok ? qrow[s * KSTEP + g] : 0.f;
+      }
+    }
+  }
+
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = f32x16{};
+  float mrow = neg_inf();  // running max of scaled scores, log2 units
+  float lsum = 0.f;        // this lane's share of the running sum
+
+  const T *kb = (const T *)p.k;
+  const T *vb = (const T *)p.v;
+
+  for (int64_t kt = it.k0; kt < it.k1; kt += kFwdBN) {
+    __syncthreads();
+    // ---- stage K and V rows [kt, kt + 64) into LDS
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ci = tid + 256 * c;
+      const int kr = ci / (D / CH);
+      const int col = (ci % (D / CH)) * CH;
+      const int64_t j = kt + kr;
+      i32x4 kv4 = {0, 0, 0, 0}, vv4 = {0, 0, 0, 0};
+      if (j < it.k1) {
+        const T *ka = key_row<T>(p, kb, p.k_st, p.k_sh, j, hk);
+        const T *va = key_row<T>(p, vb, p.v_st, p.v_sh, j, hk);
+        if (ka) kv4 = ld16(ka + col);
+        if (va) vv4 = ld16(va + col);
+      }
+      if constexpr (kBf16) {
+        st16(&sK[kr * KP + col], kv4);
+      } else {
+        float4 f = __builtin_bit_cast(float4, kv4);
+        sK[kr * KP + col + 0] = f.x; sK[kr * KP + col + 1] = f.y;
+        sK[kr * KP + col + 2] = f.z; sK[kr * KP + col + 3] = f.w;
+      }
+      st16(&sV[kr * VP + col], vv4);
+    }
+    __syncthreads();
+    if (!wave_on) continue;
+
+    // ---- per-wave skip / mask decision (wave-uniform)
+    const int64_t klast = (kt + kFwdBN <= it.k1 ? kt + kFwdBN : it.k1) - 1;
+    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
+    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
+    if (m.causal && kp_lo > wq_hi) continue;
+    if (m.window > 0 && kp_hi <= wq_lo - m.window) continue;
+    const bool full = (kt + kFwdBN <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
+                      (m.window <= 0 || kp_lo > wq_hi - m.window);
+
+    // ---- S^T = K Q^T for two 32-key sub-tiles
+    f32x16 sc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      f32x16 acc = f32x16{};
+      const T *krow = &sK[(sb * 32 + l32) * KP + g * KV];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        typename M::Frag a;
+        if constexpr (kBf16) a = *reinterpret_cast<const bf16x8 *>(krow + s * KSTEP);
+        else a = krow[s * KSTEP];
+        acc = M::mma(a, qf[s], acc);
+      }
+      sc[sb] = acc;
+    }
+    if (!full) {
+      const int32_t t0 = (int32_t)(kt - it.kdoc0);
+      const int32_t nvalid = (int32_t)(it.k1 - kt);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t kk = sb * 32 + c_row(j, lane);
+          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
+          sc[sb][j] = vis ? sc[sb][j] : neg_inf();
+        }
+      }
+    }
+    // ---- online softmax (log2 domain)
+    float mx = neg_inf();
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(mrow, mx * p.scale_log2);
+    const float muse = mnew == neg_inf() ? 0.f : mnew;
+    const float alpha = fast_exp2(mrow - muse);
+    mrow = mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], p.scale_log2, -muse));
+        sc[sb][j] = e;
+        ps += e;
+      }
+    lsum = lsum * alpha + ps;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) o[i] *= alpha;
+
+    // ---- O^T += V^T P^T
+    if constexpr (kBf16) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[t][e] = (bf16)sc[t >> 1][(t & 1) * 8 + e];
+      const int u = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int rowa = t * 16 + 4 * g + (u >> 2);
+          const int col = dt * 32 + dh * 16 + 4 * (u & 3);
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sV[rowa * VP + col]));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(&sV[(rowa + 8) * VP + col]));
+          bf16x8 va;
+          bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+          va[0] = l4[0]; va[1] = l4[1]; va[2] = l4[2]; va[3] = l4[3];
+          va[4] = h4[0]; va[5] = h4[1]; va[6] = h4[2]; va[7] = h4[3];
+          o[dt] = M::mma(va, pf[t], o[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const float a = sV[(sb * 32 + c_row(j, lane)) * VP + dt * 32 + l32];
+            o[dt] = M::mma(a, sc[sb][j], o[dt]);
+          }
+        }
+      }
+    }
+  }
+  if (!wave_on) return;
+
+  // ---- epilogue: normalise, store out and lse
+  const float lt = lsum + xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
+  if (!row_ok) return;
+  if (p.segmented) {
+    float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d0 = dt * 32 + 8 * j4 + 4 * g;
+        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
+        *reinterpret_cast<float4 *>(po + d0) = v4;
+      }
+    if (g == 0) p.part_lse[((int64_t)it.seg * p.hq + h) * p.n_q + row] = lse_v;
+    return;
+  }
+  OutT *orow = (OutT *)p.out + row * p.o_st + (int64_t)h * p.o_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      if constexpr (sizeof(OutT) == 4) {
+        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
+        *reinterpret_cast<float4 *>(orow + d0) = v4;
+      } else {
+        bf16x4 v4;
+        v4[0] = (bf16)(o[dt][4 * j4] * inv); v4[1] = (bf16)(o[dt][4 * j4 + 1] * inv);
+        v4[2] = (bf16)(o[dt][4 * j4 + 2] * inv); v4[3] = (bf16)(o[dt][4 * j4 + 3] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + d0) = v4;
+      }
+    }
+  if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid, hipStream_t s) {
+  if (out_dtype == 0)
+    hipLaunchKernelGGL((fwd_kernel<T, D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, float>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
+  FwdParams fp;
+  fp.q = a.q.data; fp.k = a.k.data; fp.v = a.v.data;
+  fp.q_st = a.q.st; fp.q_sh = a.q.sh; fp.k_st = a.k.st; fp.k_sh = a.k.sh; fp.v_st = a.v.st; fp.v_sh = a.v.sh;
+  fp.hq = a.hq; fp.group = a.hq / a.hkv;
+  fp.scale_log2 = a.scale * kLog2e;
+  fp.m = a.mask;
+  fp.block_table = a.block_table; fp.block_size = a.block_size; fp.max_blocks = a.max_blocks;
+  fp.page_stride = a.page_stride; fp.n_pages = a.n_pages;
+  fp.out = a.out; fp.o_st = a.o_st; fp.o_sh = a.o_sh;
+  fp.lse = a.lse; fp.lse_n = a.lse_n;
+  fp.segmented = a.part_out != nullptr;
+  fp.part_out = a.part_out; fp.part_lse = a.part_lse;
+  fp.n_q = a.n_q;
+  fp.items = a.sched.items; fp.order = a.sched.order; fp.count = a.sched.count;
+  const int64_t grid = a.grid_items * a.hq;
+  if (grid <= 0) return hipSuccess;
+  if (a.dtype == 0) {
+    if (a.head_dim == 128) return launch_fwd_t<bf16, 128>(fp, a.out_dtype, grid, s);
+    return launch_fwd_t<bf16, 64>(fp, a.out_dtype, grid, s);
+  }
+  if (a.head_dim == 128) return launch_fwd_t<float, 128>(fp, a.out_dtype, grid, s);
+  return launch_fwd_t<float, 64>(fp, a.out_dtype, grid, s);
+}
+
+}  // namespace attn

@@ -1,0 +1,149 @@
+// Declarations shared between the host library and the kernel translation
+// units (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace attn {
+
+// One unit of forward/backward work: a tile of query rows of one document
+// against the keys [k0, k1) it can see (already intersected with the key
+// view, the segment and the causal/window bounds).
+struct WorkItem {
+  int32_t q0, q1;      // absolute query rows [q0, q1)
+  int32_t k0, k1;      // absolute (logical) key rows [k0, k1)
+  int32_t qdoc0;       // first query row of the document
+  int32_t kdoc0;       // first key row of the document
+  int32_t seg;         // segment index (0 when not segmented)
+  int32_t cost;        // key tiles + 1, the sort key
+};
+
+// Device view of the visibility rule.
+struct MaskDev {
+  int32_t causal;
+  int32_t q_view, k_view;
+  int32_t seg_size;
+  int64_t window;
+  int64_t q_pos_offset;
+  PosMap pm;
+};
+
+struct TensorDev {
+  const void *data;
+  int64_t st, sh;  // token / head strides in elements
+};
+
+// Tile-scheduler output layout inside a workspace.
+struct SchedBufs {
+  WorkItem *items;
+  int32_t *order;
+  int32_t *count;
+  int32_t capacity;
+};
+
+constexpr int kFwdBM = 128;   // query rows per forward workgroup (4 waves x 32)
+constexpr int kFwdBN = 64;    // keys per staged tile
+constexpr int kBwdBQ = 64;    // query rows per staged tile of the dK/dV kernel
+constexpr int kBwdTile = 128; // query rows per dQ workgroup / key rows per dK-dV workgroup
+
+size_t sched_bytes(int64_t capacity);
+SchedBufs sched_carve(void *ws, int64_t capacity);
+int64_t sched_capacity(int64_t n_rows_view_bound, int32_t num_seqs, int32_t tile, int64_t n_seg);
+
+hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs,
+                           int64_t n_q, int64_t n_k, const MaskDev &m, int32_t tile,
+                           int32_t key_tile, int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s);
+
+struct FwdArgs {
+  TensorDev q, k, v;
+  int32_t dtype;         // 0 bf16, 1 f32 (q/k/v)
+  int32_t head_dim;
+  int32_t hq, hkv;
+  float scale;
+  MaskDev mask;
+  const int32_t *block_table;  // NULL = not paged
+  int32_t block_size, max_blocks;
+  int64_t page_stride, n_pages;
+  // outputs: either final (out/lse) or segment partials (part_*)
+  void *out; int32_t out_dtype; int64_t o_st, o_sh;
+  float *lse; int64_t lse_n;    // lse[h * lse_n + row]
+  float *part_out;              // [n_seg][n_q][HQ][D] f32 when segmented
+  float *part_lse;              // [n_seg][HQ][n_q]
+  int64_t n_q;
+  SchedBufs sched;
+  int64_t grid_items;           // scheduler capacity (grid bound)
+};
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  TensorDev q, k, v;
+  int32_t head_dim, hq, hkv, num_seqs;
+  float scale;
+  const int32_t *cu_q, *cu_k;
+  void *out; int32_t out_dtype; int64_t o_st, o_sh;
+  float *lse; int64_t lse_n;
+  int64_t n_k;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+struct MergeArgs {
+  float *out; int64_t o_st, o_sh;          // running f32 state
+  float *lse;
+  const void *bout; int32_t bout_dtype; int64_t b_st, b_sh;
+  const float *blse;
+  float *weight;                            // nullable
+  void *fout; int32_t fout_dtype; int64_t f_st, f_sh;  // nullable
+  const int32_t *cu; int32_t num_seqs; int32_t view;
+  int64_t n, h, d;
+  int32_t init;
+};
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+
+struct MergeNArgs {
+  int32_t n_parts;
+  int32_t strided;                 // parts = part 0 + i * (out_stride, lse_stride)
+  int64_t out_stride, lse_stride;  // elements
+  const void *pout[16]; int32_t pdtype[16]; int64_t p_st[16], p_sh[16];
+  const float *plse[16];
+  void *out; int32_t out_dtype; int64_t o_st, o_sh;
+  float *lse;
+  int64_t n, h, d;
+};
+hipError_t launch_merge_n(const MergeNArgs &a, hipStream_t s);
+
+struct DeltaArgs {
+  const void *dout; int32_t dtype_do; int64_t do_st, do_sh;
+  const void *out; int32_t dtype_o; int64_t o_st, o_sh;
+  float *delta;
+  int64_t n, h, d;
+};
+hipError_t launch_delta(const DeltaArgs &a, hipStream_t s);
+
+struct BwdArgs {
+  TensorDev q, k, v, dout;
+  int32_t dtype;
+  int32_t head_dim, hq, hkv;
+  float scale;
+  MaskDev mask;
+  const float *lse, *delta;
+  int64_t n_q, n_k;
+  float *dq; int64_t dq_st, dq_sh;
+  float *dk; int64_t dk_st, dk_sh;
+  float *dv; int64_t dv_st, dv_sh;
+  SchedBufs qsched;   // tiles of query rows (dQ kernel)
+  SchedBufs ksched;   // tiles of key rows (dK/dV kernel)
+  int64_t q_items, k_items;
+};
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
+
+hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int64_t n_src, void *dst,
+                               int64_t d_st, int64_t d_sh, int64_t n_dst, int32_t elem_bytes,
+                               int64_t heads, int64_t head_dim, const int32_t *cu, int32_t num_seqs,
+                               int32_t max_seqlen, int32_t cp, int32_t rank, hipStream_t s);
+
+hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,282 @@
+// Streaming kernels (HBM bound): online-softmax merges, the backward row term
+// delta, a float fill, and the zig-zag shard gather.
+//
+// Merge (NeMo AutoModel zigzag_ring_attention, `update_out_and_lse`;
+// ring_attention, `_update_out_and_lse` in its sigmoid form): for every
+// (row, head) of the running state
+//     lse' = max + log1p(exp(-|lse - block_lse|))
+//     sigma = exp(block_lse - lse')          (= sigmoid(block_lse - lse))
+//     out' = out - sigma * (out - block_out)
+// A group of D/4 lanes owns one (row, head): each lane moves 16 bytes of the
+// f32 running output, so a wave streams two or four contiguous 512-byte rows.
+#include "internal.h"
+
+namespace attn {
+
+template <typename T> __device__ __forceinline__ f32x4 ld4(const T *p);
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+template <> __device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+template <typename T> __device__ __forceinline__ void st4(T *p, f32x4 v);
+template <> __device__ __forceinline__ void st4<float>(float *p, f32x4 v) {
+  *reinterpret_cast<f32x4 *>(p) = v;
+}
+template <> __device__ __forceinline__ void st4<bf16>(bf16 *p, f32x4 v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4 *>(p) = b;
+}
+
+// Is `row` inside the view of its document? (binary search over cu)
+__device__ __forceinline__ bool row_in_view(const int32_t *cu, int32_t num_seqs, int view, int64_t row) {
+  if (view == 0) return true;
+  int lo = 0, hi = num_seqs;  // find d with cu[d] <= row < cu[d+1]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int64_t s = cu[lo], e = cu[lo + 1];
+  if (row < s || row >= e) return false;
+  const int64_t h = (e - s) / 2;
+  return view == 1 ? row < s + h : row >= s + h;
+}
+
+template <int D, typename BT, typename FT>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int G = D / 4;  // lanes per (row, head)
+  const int64_t total = a.n * a.h;
+  const int sub = threadIdx.x % G;
+  const int64_t per_blk = 256 / G;
+  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
+    const int64_t row = pr / a.h;
+    const int64_t h = pr - row * a.h;
+    const int64_t li = h * a.n + row;
+    if (!row_in_view(a.cu, a.num_seqs, a.view, row)) {
+      // rows outside the view keep their state; a final cast still covers them
+      if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub,
+                          ld4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub));
+      continue;
+    }
+    const float lb = a.blse[li];
+    const f32x4 bo = ld4<BT>((const BT *)a.bout + row * a.b_st + h * a.b_sh + 4 * sub);
+    float ln, sig;
+    f32x4 res;
+    if (a.init) {
+      ln = lb; sig = 1.f; res = bo;
+    } else {
+      const float la = a.lse[li];
+      const f32x4 oa = ld4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub);
+      const float mx = fmaxf(la, lb);
+      // an empty partial (lse = -inf) has weight 0, whatever its out holds
+      if (mx == neg_inf()) {
+        ln = neg_inf(); sig = 0.f; res = f32x4{};
+      } else if (la == neg_inf()) {
+        ln = lb; sig = 1.f; res = bo;
+      } else if (lb == neg_inf()) {
+        ln = la; sig = 0.f; res = oa;
+      } else {
+        ln = mx + log1pf(expf(-fabsf(la - lb)));
+        sig = expf(lb - ln);
+        res = oa - sig * (oa - bo);
+      }
+    }
+    if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub, res);
+    else st4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub, res);
+    if (sub == 0) {
+      a.lse[li] = ln;
+      if (a.weight) a.weight[li] = sig;
+    }
+  }
+}
+
+static unsigned stream_grid(int64_t pairs, int per_blk) {
+  int64_t b = (pairs + per_blk - 1) / per_blk;
+  const int64_t cap = 256 * 32;  // enough waves to saturate HBM, grid-stride beyond
+  if (b > cap) b = cap;
+  return (unsigned)(b < 1 ? 1 : b);
+}
+
+template <int D, typename BT>
+static void launch_merge_b(const MergeArgs &a, hipStream_t s, unsigned grid) {
+  if (a.fout && a.fout_dtype == 0)
+    hipLaunchKernelGGL((merge_kernel<D, BT, bf16>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, BT, float>), dim3(grid), dim3(256), 0, s, a);
+}
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
+  if (a.n * a.h == 0) return hipSuccess;
+  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  if (a.d == 128) {
+    if (a.bout_dtype == 0) launch_merge_b<128, bf16>(a, s, grid);
+    else launch_merge_b<128, float>(a, s, grid);
+  } else {
+    if (a.bout_dtype == 0) launch_merge_b<64, bf16>(a, s, grid);
+    else launch_merge_b<64, float>(a, s, grid);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// R-way merge (AWS NKI "Attention KV-Parallel Segmented CTE", Background:
+// the partials of the ranks are combined by online softmax):
+//   lse = m + log(sum_i exp(lse_i - m)),  out = sum_i exp(lse_i - lse) out_i
+// ---------------------------------------------------------------------------
+template <int D, typename OT>
+__global__ __launch_bounds__(256) void merge_n_kernel(MergeNArgs a) {
+  constexpr int G = D / 4;
+  const int64_t total = a.n * a.h;
+  const int sub = threadIdx.x % G;
+  const int64_t per_blk = 256 / G;
+  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
+    const int64_t row = pr / a.h;
+    const int64_t h = pr - row * a.h;
+    const int64_t li = h * a.n + row;
+    // part i: explicit pointers, or (strided) part 0 advanced by i strides
+    auto plse = [&](int i) -> float {
+      return a.strided ? a.plse[0][li + i * a.lse_stride] : a.plse[i][li];
+    };
+    float mx = neg_inf();
+    for (int i = 0; i < a.n_parts; ++i) mx = fmaxf(mx, plse(i));
+    f32x4 acc = f32x4{};
+    float ln = neg_inf();
+    if (mx != neg_inf()) {
+      float z = 0.f;
+      for (int i = 0; i < a.n_parts; ++i) z += expf(plse(i) - mx);
+      ln = mx + logf(z);
+      for (int i = 0; i < a.n_parts; ++i) {
+        const float wgt = expf(plse(i) - ln);
+        if (wgt == 0.f) continue;
+        const int pi = a.strided ? 0 : i;
+        const int64_t off = a.strided ? i * a.out_stride : 0;
+        f32x4 v = a.pdtype[pi] == 0
+                      ? ld4<bf16>((const bf16 *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub)
+                      : ld4<float>((const float *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub);
+        acc += wgt * v;
+      }
+    }
+    st4<OT>((OT *)a.out + row * a.o_st + h * a.o_sh + 4 * sub, acc);
+    if (sub == 0) a.lse[li] = ln;
+  }
+}
+
+hipError_t launch_merge_n(const MergeNArgs &a, hipStream_t s) {
+  if (a.n * a.h == 0) return hipSuccess;
+  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  if (a.d == 128) {
+    if (a.out_dtype == 0) hipLaunchKernelGGL((merge_n_kernel<128, bf16>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((merge_n_kernel<128, float>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (a.out_dtype == 0) hipLaunchKernelGGL((merge_n_kernel<64, bf16>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((merge_n_kernel<64, float>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// delta[h, i] = sum_d dout[i,h,d] * out[i,h,d] with the merged out (NeMo
+// AutoModel zigzag_ring_attention, `zigzag_ring_flash_attn_varlen_backward`:
+// every block's backward sees the final merged out, so this row term is the
+// same for all blocks and is computed once).
+// ---------------------------------------------------------------------------
+template <int D, typename T1, typename T2>
+__global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
+  constexpr int G = D / 4;
+  const int64_t total = a.n * a.h;
+  const int sub = threadIdx.x % G;
+  const int64_t per_blk = 256 / G;
+  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
+    const int64_t row = pr / a.h;
+    const int64_t h = pr - row * a.h;
+    const f32x4 x = ld4<T1>((const T1 *)a.dout + row * a.do_st + h * a.do_sh + 4 * sub);
+    const f32x4 y = ld4<T2>((const T2 *)a.out + row * a.o_st + h * a.o_sh + 4 * sub);
+    float v = x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (sub == 0) a.delta[h * a.n + row] = v;
+  }
+}
+
+template <int D>
+static void launch_delta_d(const DeltaArgs &a, hipStream_t s, unsigned grid) {
+  if (a.dtype_do == 0 && a.dtype_o == 0) hipLaunchKernelGGL((delta_kernel<D, bf16, bf16>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.dtype_do == 0) hipLaunchKernelGGL((delta_kernel<D, bf16, float>), dim3(grid), dim3(256), 0, s, a);
+  else if (a.dtype_o == 0) hipLaunchKernelGGL((delta_kernel<D, float, bf16>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((delta_kernel<D, float, float>), dim3(grid), dim3(256), 0, s, a);
+}
+
+hipError_t launch_delta(const DeltaArgs &a, hipStream_t s) {
+  if (a.n * a.h == 0) return hipSuccess;
+  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  if (a.d == 128) launch_delta_d<128>(a, s, grid);
+  else launch_delta_d<64>(a, s, grid);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ void fill_kernel(float *p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t b = (n + 255) / 256;
+  if (b > 8192) b = 8192;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)b), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Zig-zag shard (NeMo AutoModel zigzag_ring_attention, module docstring and
+// `get_half_index`): per document of L rows and chunk c = L / (2 cp), local
+// row t of rank r is global row  start + r*c + t            (t <  c)
+//                                start + (2cp-1-r)*c + t - c  (t >= c).
+// One wave copies one local row (all heads) in 16-byte pieces.
+// ---------------------------------------------------------------------------
+struct ShardParams {
+  const char *src; int64_t s_st, s_sh;
+  char *dst; int64_t d_st, d_sh;
+  int32_t eb; int64_t heads, row_bytes;
+  const int32_t *cu; int32_t cp, rank;
+  int64_t n_src, n_dst;
+};
+
+__global__ __launch_bounds__(256) void zigzag_shard_kernel(ShardParams p) {
+  const int doc = blockIdx.y;
+  const int64_t gs = p.cu[doc], ge = p.cu[doc + 1];
+  const int64_t L = ge - gs;
+  const int64_t c = L / (2 * p.cp);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= 2 * c) return;
+  const int64_t grow = t < c ? gs + p.rank * c + t : gs + (2 * p.cp - 1 - p.rank) * c + (t - c);
+  const int64_t lrow = gs / p.cp + t;
+  if (grow < 0 || grow >= p.n_src || lrow < 0 || lrow >= p.n_dst) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t per_head = p.row_bytes / p.heads;  // bytes of one head (D * eb)
+  for (int64_t off = lane * 16; off < p.row_bytes; off += 64 * 16) {
+    const int64_t hh = off / per_head, dd = off - hh * per_head;
+    const char *s = p.src + (grow * p.s_st + hh * p.s_sh) * p.eb + dd;
+    char *d = p.dst + (lrow * p.d_st + hh * p.d_sh) * p.eb + dd;
+    st16(d, ld16(s));
+  }
+}
+
+hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int64_t n_src, void *dst,
+                               int64_t d_st, int64_t d_sh, int64_t n_dst, int32_t elem_bytes,
+                               int64_t heads, int64_t head_dim, const int32_t *cu, int32_t num_seqs,
+                               int32_t max_seqlen, int32_t cp, int32_t rank, hipStream_t s) {
+  if (num_seqs <= 0) return hipSuccess;
+  ShardParams p{(const char *)src, s_st, s_sh, (char *)dst, d_st, d_sh, elem_bytes, heads,
+                heads * head_dim * elem_bytes, cu, cp, rank, n_src, n_dst};
+  const int64_t max_local = max_seqlen / cp;  // 2c for the longest document
+  const unsigned gx = (unsigned)((max_local + 3) / 4);
+  if (gx == 0) return hipSuccess;
+  hipLaunchKernelGGL(zigzag_shard_kernel, dim3(gx, (unsigned)num_seqs), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -231,7 +231,7 @@ def merge(out_a, lse_a, out_b, lse_b):
     return out, lse, wb
 
 
-def block_backward(dout, q, k, v, out, lse, cu_q, cu_k, scale, chunk=1024, **mask):
+def block_backward(dout, q, k, v, out, lse, cu_q, cu_k, scale, chunk=1024, rows=None, krows=None, **mask):
     """Gradient contribution of one block, given the MERGED out and lse.
 
     [ZZ] `zigzag_ring_flash_attn_varlen_backward`: every block's backward is fed
@@ -245,6 +245,9 @@ def block_backward(dout, q, k, v, out, lse, cu_q, cu_k, scale, chunk=1024, **mas
         dk_j   += scale sum_{i, h in group} dS_ij q_i
         dv_j   += sum_{i, h in group} P_ij dout_i
     Returns (dq [n_q,HQ,D], dk [n_k,HKV,D], dv [n_k,HKV,D]).
+    ``rows`` / ``krows`` evaluate the same sums for a sample: only the listed
+    query rows (exact dq for them) or only the listed key rows (exact dk/dv
+    for them) take part; the other outputs are then partial.
     """
     m = _mask_args(mask)
     dout, q, k, v, out = (as_f64(t) for t in (dout, q, k, v, out))
@@ -257,7 +260,9 @@ def block_backward(dout, q, k, v, out, lse, cu_q, cu_k, scale, chunk=1024, **mas
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for d in range(len(doc_bounds(cu_q))):
-        qs, ks, qi, kj = _doc_rows(cu_q, cu_k, d, m["q_view"], m["k_view"], None, m.get("k_range"))
+        qs, ks, qi, kj = _doc_rows(cu_q, cu_k, d, m["q_view"], m["k_view"], rows, m.get("k_range"))
+        if krows is not None:
+            kj = kj[np.isin(kj, krows)]
         if len(qi) == 0 or len(kj) == 0:
             continue
         qpos, kpos = _positions(qs, ks, qi, kj, m)
@@ -505,7 +510,7 @@ def kvp_global_kv(caches, tables, n_blocks, interleave=True):
 
 
 def kvp_rank_partial(q, k_cache, v_cache, block_table, n_blocks, R, r, seg_size, global_q_offset,
-                     window, scale, interleave=True, causal=True):
+                     window, scale, interleave=True, causal=True, rows=None):
     """One rank's partial (out, lse) over its local KV, segment by segment.
 
     [KVP] Background: each rank attends its local KV shard in segments of
@@ -525,7 +530,7 @@ def kvp_rank_partial(q, k_cache, v_cache, block_table, n_blocks, R, r, seg_size,
     seg = seg_size if seg_size else nk
     out = lse = None
     for a in range(0, nk, seg):
-        bo, bl = block_forward(q, k, v, cu_q, cu_k, scale, causal=causal, window=window,
+        bo, bl = block_forward(q, k, v, cu_q, cu_k, scale, rows=rows, causal=causal, window=window,
                                q_pos_offset=global_q_offset, k_range=(a, a + seg), **pos)
         if out is None:
             out, lse = bo, bl
@@ -535,12 +540,12 @@ def kvp_rank_partial(q, k_cache, v_cache, block_table, n_blocks, R, r, seg_size,
 
 
 def kvp_forward(q, k_caches, v_caches, tables, n_blocks, seg_size, global_q_offset, window, scale,
-                interleave=True):
+                interleave=True, rows=None):
     """[KVP] merged output: the R ranks' partials merged by online softmax
-    (rank order 0..R-1). Returns (out, lse, partials)."""
+    (rank order 0..R-1). Returns (out, lse, partials). q is [S, HQ, D]."""
     R = len(k_caches)
     parts = [kvp_rank_partial(q, k_caches[r], v_caches[r], tables[r], n_blocks, R, r, seg_size,
-                              global_q_offset, window, scale, interleave) for r in range(R)]
+                              global_q_offset, window, scale, interleave, rows=rows) for r in range(R)]
     out, lse = parts[0]
     for r in range(1, R):
         out, lse, _ = merge(out, lse, *parts[r])
