@@ -14,7 +14,8 @@ order lengths -> q -> k -> v -> dout -> block tables):
     stop when the next document would reach or pass the total, and the last
     document takes the remainder (itself a multiple of `multiple`);
   * the decode workload's K/V (~137 GB) are drawn on the GPU with a CUDA
-    generator seeded 0, in the order k then v.
+    generator seeded 0, k then v, each in chunks of 2^20 rows of fp32 draws
+    rounded to bf16.
 """
 
 from __future__ import annotations
@@ -35,6 +36,17 @@ def normal(shape, dtype, gen, device="cpu") -> torch.Tensor:
     """N(0,1) in float32, then cast (RNE for bf16)."""
     x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=device)
     return x if dtype == torch.float32 else x.to(dtype)
+
+
+def normal_chunked(shape, gen, device, rows_per_chunk=1 << 20):
+    """bf16 N(0,1) drawn on the device in row chunks of fp32 draws (bounded
+    temporary memory for the ~137 GB decode K/V)."""
+    out = torch.empty(*shape, dtype=torch.bfloat16, device=device)
+    for a in range(0, shape[0], rows_per_chunk):
+        b = min(shape[0], a + rows_per_chunk)
+        out[a:b] = torch.randn((b - a,) + tuple(shape[1:]), generator=gen, dtype=torch.float32,
+                               device=device).to(torch.bfloat16)
+    return out
 
 
 def _finish(lengths, total):
@@ -197,9 +209,10 @@ def cfg5(device="cpu", nseq=65536, max_len=2048, hq=32, hkv=4, d=128, seed=0):
     if str(device).startswith("cuda"):
         gd = torch.Generator(device=device)
         gd.manual_seed(seed)
+        k = normal_chunked((total, hkv, d), gd, device)
+        v = normal_chunked((total, hkv, d), gd, device)
     else:
-        gd = g
-    k = normal((total, hkv, d), torch.bfloat16, gd, device=device)
-    v = normal((total, hkv, d), torch.bfloat16, gd, device=device)
+        k = normal((total, hkv, d), torch.bfloat16, g)
+        v = normal((total, hkv, d), torch.bfloat16, g)
     scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     return DecodeCase(q.to(device), k, v, cu.to(torch.int32), lens, scale)

@@ -1,0 +1,184 @@
+"""Device-side set-up of the five workloads and their exact work counts.
+
+Each workload places the seeded inputs (blockwise_causal_varlen_amd.inputs) on
+the GPU, lays them out the way the virtual ranks hold them (the zig-zag shard
+runs in the library's kernel), and exposes `forward()` / `backward()` steps
+that call only the C ABI. The counting helpers give the algorithmic work the
+roofline figures are priced on: visible (query, key) pairs per q head, from
+closed forms and integer position arithmetic (no attention math).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import inputs as I
+from . import lib as L
+
+
+# ----------------------------------------------------------------------------
+# exact counts
+# ----------------------------------------------------------------------------
+def zigzag_rank_pairs(doc_lens, cp):
+    """Visible pairs per q head of ONE zig-zag rank over all cp steps (equal
+    for every rank). Per document with chunk c = L / (2 cp): the causal block
+    over the rank's 2c rows has c (2c + 1) pairs and each of the cp - 1 other
+    steps (front keys or back queries) has 2 c^2."""
+    tot = 0
+    for L_ in doc_lens:
+        c = L_ // (2 * cp)
+        tot += c * (2 * c + 1) + (cp - 1) * 2 * c * c
+    return tot
+
+
+def zigzag_step_pairs(doc_lens, cp, step):
+    tot = 0
+    for L_ in doc_lens:
+        c = L_ // (2 * cp)
+        tot += c * (2 * c + 1) if step == 0 else 2 * c * c
+    return tot
+
+
+def kvp_rank_pairs(s_q, global_q_offset, n_local, R, r, block_size, window):
+    """Visible pairs per q head of KV-parallel rank r (round-robin keys)."""
+    qpos = global_q_offset + np.arange(s_q, dtype=np.int64)
+
+    def count_le(p):  # local keys with position <= p
+        p = np.asarray(p, dtype=np.int64)
+        blk, off = p // block_size, p % block_size
+        nb = n_local // block_size
+        # local blocks b with b*R + r < blk are fully <= p; block b*R + r == blk partly
+        full = np.clip((blk - r + R - 1) // R, 0, nb)  # count of b with b*R + r < blk
+        part = np.where(((blk - r) % R == 0) & (blk >= r) & ((blk - r) // R < nb), off + 1, 0)
+        return np.minimum(full * block_size + part, n_local)
+
+    hi = count_le(qpos)
+    lo = count_le(qpos - window) if window > 0 else np.zeros_like(hi)
+    return int(np.sum(np.maximum(hi - lo, 0)))
+
+
+def decode_bytes(k_lens, hq, hkv, d):
+    """Algorithmic HBM bytes of one decode pass: K and V once per kv head,
+    q and out (bf16), lse (f32), cu_seqlens (int32)."""
+    nseq = len(k_lens)
+    kv = int(np.sum(np.asarray(k_lens, dtype=np.int64))) * hkv * d * 2 * 2
+    return kv + nseq * hq * d * 2 * 2 + nseq * hq * 4 + (2 * nseq + 2) * 4
+
+
+# ----------------------------------------------------------------------------
+# zig-zag
+# ----------------------------------------------------------------------------
+class ZigzagWorkload:
+    """cp virtual zig-zag ranks; `ranks` are the ones that run (all by default)."""
+
+    def __init__(self, case: I.ZigzagCase, ranks=None, device="cuda", with_bwd=False):
+        self.case, self.cp = case, case.cp
+        cp = case.cp
+        self.ranks = list(range(cp)) if ranks is None else list(ranks)
+        self.device = device
+        cu = case.cu
+        self.doc_lens = (cu[1:] - cu[:-1]).tolist()
+        self.max_len = int(max(self.doc_lens))
+        self.max_local = self.max_len // cp
+        self.cu_global = cu.to(device)
+        self.cu_local = (cu // cp).to(torch.int32).to(device)
+        k, v = case.k.to(device), case.v.to(device)
+        self.k_loc = [L.zigzag_shard(k, self.cu_global, cp, r, self.max_len) for r in range(cp)]
+        self.v_loc = [L.zigzag_shard(v, self.cu_global, cp, r, self.max_len) for r in range(cp)]
+        del k, v
+        self.q_loc, self.dout_loc, self.runners = {}, {}, {}
+        for r in self.ranks:
+            if case.q_rank is not None:
+                if r != case.q_rank:
+                    raise ValueError("this case holds q for one rank only")
+                q = case.q.to(device)
+                do = case.dout.to(device) if (with_bwd and case.dout is not None) else None
+            else:
+                q = L.zigzag_shard(case.q.to(device), self.cu_global, cp, r, self.max_len)
+                do = (L.zigzag_shard(case.dout.to(device), self.cu_global, cp, r, self.max_len)
+                      if (with_bwd and case.dout is not None) else None)
+            self.q_loc[r], self.dout_loc[r] = q, do
+            self.runners[r] = L.RingRunner("zigzag", cp, r, q, self.k_loc, self.v_loc, self.cu_local,
+                                           self.max_local, case.scale, dout=do)
+
+    def forward(self):
+        for r in self.ranks:
+            self.runners[r].forward()
+
+    def backward(self):
+        for r in self.ranks:
+            self.runners[r].zero_grads()
+            self.runners[r].backward()
+
+    def pairs_per_rank(self):
+        return zigzag_rank_pairs(self.doc_lens, self.cp)
+
+    def fwd_flops(self):
+        hq, d = self.case.q.shape[1], self.case.q.shape[2]
+        return 4 * d * hq * self.pairs_per_rank() * len(self.ranks)
+
+    def bwd_flops(self):
+        hq, d = self.case.q.shape[1], self.case.q.shape[2]
+        return 10 * d * hq * self.pairs_per_rank() * len(self.ranks)
+
+
+# ----------------------------------------------------------------------------
+# KV-parallel
+# ----------------------------------------------------------------------------
+class KvpWorkload:
+    def __init__(self, case: I.KvpCase, device="cuda"):
+        self.case = case
+        self.q = case.q.to(device)                      # [H, S, D]
+        self.q_shd = self.q.transpose(0, 1)             # [S, H, D] view
+        self.kc = [c.to(device) for c in case.k_caches]
+        self.vc = [c.to(device) for c in case.v_caches]
+        self.tabs = [t.reshape(-1).to(device) for t in case.tables]
+        hq, s_q, d = case.q.shape
+        self.s_q, self.hq, self.d = s_q, hq, d
+        self.n_blocks = case.tables[0].numel()
+        self.n_local = self.n_blocks * case.block_size
+        self.cu_q = torch.tensor([0, s_q], dtype=torch.int32, device=device)
+        self.cu_k = torch.tensor([0, self.n_local], dtype=torch.int32, device=device)
+        self.mask = L.mask(causal=True, window=case.window, q_pos_offset=case.global_q_offset,
+                           kv_interleave=case.R, block_size=case.block_size, max_blocks=self.n_blocks,
+                           page_stride=self.kc[0].stride(0), seg_size=case.seg_size,
+                           block_table=self.tabs[0])
+        self.out = torch.empty(s_q, hq, d, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(hq, s_q, dtype=torch.float32, device=device)
+
+    def forward(self):
+        return L.kvp_fwd(self.q_shd, self.kc, self.vc, self.tabs, self.cu_q, self.cu_k, self.s_q, self.n_local,
+                         self.case.scale, self.mask, out=self.out, lse=self.lse)
+
+    def pairs(self):
+        c = self.case
+        return sum(kvp_rank_pairs(self.s_q, c.global_q_offset, self.n_local, c.R, r, c.block_size, c.window)
+                   for r in range(c.R))
+
+    def fwd_flops(self):
+        return 4 * self.d * self.hq * self.pairs()
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+class DecodeWorkload:
+    def __init__(self, case: I.DecodeCase, device="cuda"):
+        self.case = case
+        nseq, hq, d = case.q.shape
+        self.nseq, self.hq, self.d, self.hkv = nseq, hq, d, case.k.shape[1]
+        self.q = case.q.to(device)
+        self.k, self.v = case.k.to(device), case.v.to(device)
+        self.cu_q = torch.arange(nseq + 1, dtype=torch.int32, device=device)
+        self.cu_k = case.cu_k.to(device)
+        self.max_k = int(case.k_lens.max())
+        self.out = torch.empty(nseq, hq, d, dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty(hq, nseq, dtype=torch.float32, device=device)
+
+    def forward(self):
+        return L.block_fwd(self.q, self.k, self.v, self.cu_q, self.cu_k, 1, self.max_k, self.case.scale, None,
+                           out=self.out, lse=self.lse)
+
+    def bytes(self):
+        return decode_bytes(self.case.k_lens.numpy(), self.hq, self.hkv, self.d)

@@ -312,10 +312,11 @@ def zigzag_shard(x, cu, cp, r):
     document ([ZZ] `get_half_index` works per varlen document), so each local
     document is [chunk r | chunk 2cp-1-r] and local cu_seqlens = global / cp.
     """
+    x = as_f64(x)
     parts = []
     for s, e in doc_bounds(cu):
         for a, b in _zz_chunks(e - s, cp, r):
-            parts.append(np.asarray(x[s + a:s + b]))
+            parts.append(x[s + a:s + b])
     local = np.concatenate(parts, axis=0)
     return local, np.asarray(cu, dtype=np.int64) // cp
 
@@ -443,12 +444,13 @@ def zigzag_backward(dout_r, q_loc, k_loc, v_loc, out_r, lse_r, cu_global, cp, r,
 def ring_shard(x, cu, cp, r):
     """Rank r's contiguous shard of every sequence: rows [r*S/cp, (r+1)*S/cp)
     of each one ([RING] module docstring: each rank holds a contiguous S/cp)."""
+    x = as_f64(x)
     parts = []
     for s, e in doc_bounds(cu):
         if (e - s) % cp:
             raise ValueError("sequence length not divisible by cp")
         n = (e - s) // cp
-        parts.append(np.asarray(x[s + r * n:s + (r + 1) * n]))
+        parts.append(x[s + r * n:s + (r + 1) * n])
     return np.concatenate(parts, axis=0), np.asarray(cu, dtype=np.int64) // cp
 
 
@@ -501,7 +503,7 @@ def kvp_global_kv(caches, tables, n_blocks, interleave=True):
     loc = [kvp_gather_pages(c, t, n_blocks) for c, t in zip(caches, tables)]
     if not interleave:
         return np.concatenate(loc, axis=0)
-    bs = np.asarray(caches[0]).shape[2]
+    bs = caches[0].shape[2]
     blocks = []
     for b in range(n_blocks):
         for r in range(R):
@@ -520,10 +522,11 @@ def kvp_rank_partial(q, k_cache, v_cache, block_table, n_blocks, R, r, seg_size,
     `kvp_q_offset = -rank*local_kv_len + global_q_offset` expresses when the
     offset is moved to the query side). Segments are merged in order.
     """
+    q = as_f64(q)
     k = kvp_gather_pages(k_cache, block_table, n_blocks)
     v = kvp_gather_pages(v_cache, block_table, n_blocks)
-    nq, nk = np.asarray(q).shape[0], k.shape[0]
-    bs = np.asarray(k_cache).shape[2]
+    nq, nk = q.shape[0], k.shape[0]
+    bs = k_cache.shape[2]
     cu_q, cu_k = [0, nq], [0, nk]
     pos = (dict(kv_interleave=R, kv_rank=r, block_size=bs) if interleave
            else dict(k_pos_offset=r * nk))
@@ -559,7 +562,7 @@ def decode_forward(q, k, v, cu_k, scale, seqs=None):
     """[DEC] one query row per sequence (cu_seqlens_q = arange), a variable
     number of gathered key rows each, GQA, no mask. ``seqs`` selects a sample
     of sequences; other rows come back as out 0, lse -inf."""
-    nq = np.asarray(q).shape[0] if not hasattr(q, "shape") else q.shape[0]
+    nq = q.shape[0]
     cu_q = np.arange(nq + 1)
     if seqs is None:
         return block_forward(q, k, v, cu_q, cu_k, scale)
