@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise causal varlen attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|headline]
+
+A step is one pass of the hot path over the headline workload: one zig-zag
+virtual rank of a cp=8 ring at its real shape (rank 3 of 131072 packed tokens,
+log-uniform documents in [1024, 32768], 16384 local rows, HQ=32, HKV=8,
+D=128, bf16): the 8 forward blocks in ring order with their 7 online-softmax
+merges (the last one fused with the bf16 cast), then the backward: delta once
+and the 8 merged-lse block backwards accumulating dq and every owner's dk/dv.
+The metric is causal-effective TFLOP/s of forward + backward: visible pairs x
+(4 + 10) x D x HQ per step over the timed wall time (masked work never
+counts). Inputs are resident in HBM before timing starts.
+
+The JSON line also carries
+  * roofline: the dominant kernel's algorithmic FLOPs (or bytes) per launch
+    over its mean launch duration, from hipEvents the library records around
+    its own launches on their stream during the timed steps, against the
+    MI355X peak (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s);
+  * kernels: the same for every kernel of the step;
+  * rows: the other workloads of the path measured the same way (packed
+    varlen forward over 4 ranks, KV-parallel paged prefill for both windows,
+    one-query decode GB/s) -- skipped with --rows headline;
+  * cpu_baseline: the fp64 oracle timed on the host on a bounded sample of
+    the same workload (sampled query rows, forward and backward).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (AMD published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD published)
+METRIC = "causal-effective TFLOP/s fwd(+bwd) & % bf16 MFMA peak; decode GB/s & % HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "blockwise_causal_varlen_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    record matches the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#") or "=" not in line:
+            continue
+        k, v = line.split("=", 1)
+        rec[k.strip()] = v.strip()
+    if rec.get("sources") != sources_digest():
+        return None
+    v = rec.get(f"{kernel}.bytes_per_launch")
+    return float(v) if v else None
+
+
+def timed_steps(step, steps, warmup, torch, lib, timing=True):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if timing:
+        lib.attn_timing_enable(True)
+        lib.attn_timing_report()  # clear
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = {}
+    if timing:
+        kt = lib.attn_timing_report()
+        lib.attn_timing_enable(False)
+    return (t1 - t0) / steps, kt
+
+
+def roofline(name, work_per_step, kt, steps, bound, traffic=None):
+    """achieved = algorithmic work of all launches / their summed durations."""
+    cnt, ms = kt.get(name, (0, 0.0))
+    if cnt == 0 or ms <= 0:
+        return None
+    per_launch = work_per_step * steps / cnt
+    mean_s = ms / 1e3 / cnt
+    if bound == "mfma":
+        achieved = per_launch / mean_s / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = per_launch / mean_s / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "launches_per_step": cnt / steps,
+            "mean_launch_us": round(mean_s * 1e6, 2), "work_per_launch": per_launch}
+
+
+def headline(args, torch, lib, I, W):
+    case = I.cfg3(rank=3)
+    cp, r = case.cp, 3
+    nloc, hq, d = case.q.shape
+    wl = W.ZigzagWorkload(case, ranks=[r], with_bwd=True)
+
+    def step():
+        wl.forward()
+        wl.backward()
+
+    sec, kt = timed_steps(step, args.steps, args.warmup, torch, lib)
+    pairs = wl.pairs_per_rank()
+    fwd_f, bwd_f = 4 * d * hq * pairs, 10 * d * hq * pairs
+    tflops = (fwd_f + bwd_f) / sec / 1e12
+    # algorithmic bytes of the merges: (row, head) units per step, 1292 B each
+    # (f32 out read+write 1024, bf16 block out 256, lse 3 x 4) except the last,
+    # fused with the bf16 cast (view rows 1036 B, other rows 768 B)
+    doc_lens = wl.doc_lens
+    rows_all = sum(L_ // cp for L_ in doc_lens)
+    rows_back = sum(L_ // (2 * cp) for L_ in doc_lens)
+    merge_units = []
+    for s in range(1, cp):
+        view_rows = rows_all if s <= r else rows_back
+        last = s == cp - 1
+        b = view_rows * hq * (1036 if last else 1292)
+        if last:
+            b += (rows_all - view_rows) * hq * 768
+        merge_units.append(b)
+    merge_bytes = sum(merge_units)
+    delta_bytes = rows_all * hq * (256 + 256 + 4)
+    kernels = {
+        "attn_fwd": roofline("attn_fwd", fwd_f, kt, args.steps, "mfma", load_traffic("attn_fwd")),
+        "attn_dkdv": roofline("attn_dkdv", 8 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dkdv")),
+        "attn_dq": roofline("attn_dq", 2 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dq")),
+        "attn_merge": roofline("attn_merge", merge_bytes, kt, args.steps, "hbm", load_traffic("attn_merge")),
+        "attn_delta": roofline("attn_delta", delta_bytes, kt, args.steps, "hbm", load_traffic("attn_delta")),
+    }
+    times = {k: v[1] for k, v in kt.items()}
+    dominant = max((k for k in kernels if kernels[k]), key=lambda k: times.get(k, 0.0))
+    cfg = {"workload": "zigzag cp=8, virtual rank 3 of 131072 packed tokens (16384 local rows), fwd 8 blocks + "
+                       "7 merges + bwd (delta + 8 merged-lse blocks)",
+           "tokens_global": 131072, "local_rows": nloc, "docs": len(doc_lens), "hq": hq, "hkv": 8, "head_dim": d,
+           "cp": cp, "rank": r, "visible_pairs_per_head": pairs,
+           "flops_fwd": fwd_f, "flops_bwd": bwd_f, "parallelism": "one virtual rank on one GPU"}
+    return {"ms_per_step": sec * 1e3, "value": tflops, "fwd_flops": fwd_f, "bwd_flops": bwd_f, "pairs": pairs,
+            "kernels": kernels, "dominant": dominant, "kernel_ms": kt, "config": cfg, "wl": wl, "case": case}
+
+
+def other_rows(args, torch, lib, I, W):
+    rows = {}
+    steps = max(3, args.steps // 2)
+    # packed varlen forward, 4 zig-zag ranks (all of them)
+    c2 = I.cfg2()
+    w2 = W.ZigzagWorkload(c2)
+    sec, kt = timed_steps(w2.forward, steps, args.warmup, torch, lib)
+    f = w2.fwd_flops()
+    rows["packed_varlen_fwd_cp4"] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12, "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+                                     "fwd_kernel": roofline("attn_fwd", f, kt, steps, "mfma")}
+    del w2, c2
+    for window in (0, 4096):
+        c4 = I.cfg4(window=window)
+        w4 = W.KvpWorkload(c4)
+        sec, kt = timed_steps(w4.forward, steps, args.warmup, torch, lib)
+        f = w4.fwd_flops()
+        R, n, hq, d = c4.R, w4.s_q, w4.hq, w4.d
+        merge_bytes = n * hq * (R * (d * 4 + 4) + d * 2 + 4)
+        rows[f"kvp_prefill_W{window}"] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12,
+                                          "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+                                          "fwd_kernel": roofline("attn_fwd", f, kt, steps, "mfma"),
+                                          "rank_merge": roofline("attn_merge_n", merge_bytes, kt, steps, "hbm"),
+                                          "kernel_ms": kt}
+        del w4, c4
+    torch.cuda.empty_cache()
+    c5 = I.cfg5(device="cuda")
+    w5 = W.DecodeWorkload(c5)
+    sec, kt = timed_steps(w5.forward, steps, 1, torch, lib)
+    b = w5.bytes()
+    rows["decode_65536"] = {"ms": sec * 1e3, "GB/s": b / sec / 1e9, "frac": b / sec / 1e9 / PEAK_HBM_GBS,
+                            "bytes": b, "decode_kernel": roofline("attn_decode", b, kt, steps, "hbm",
+                                                                  load_traffic("attn_decode"))}
+    del w5, c5
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(case, target_s, np):
+    """fp64 oracle on sampled query rows of the headline workload: the 8
+    forward blocks + merges and the 8 backward blocks for those rows."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    from blockwise_causal_varlen_amd import workloads as W
+
+    cp, r = case.cp, 3
+    cu = case.cu
+    cu_l = (cu // cp).numpy()
+    ks = [O.zigzag_shard(case.k, cu, cp, s)[0] for s in range(cp)]
+    vs = [O.zigzag_shard(case.v, cu, cp, s)[0] for s in range(cp)]
+    q, do = O.as_f64(case.q), O.as_f64(case.dout)
+    rng = np.random.default_rng(0)
+
+    def run(nrows):
+        rows = np.sort(rng.choice(q.shape[0], nrows, replace=False))
+        t0 = time.perf_counter()
+        out = lse = None
+        for s in range(cp):
+            src, kind = O.zigzag_step(r, s, cp)
+            bo, bl = O.block_forward(q, ks[src], vs[src], cu_l, cu_l, case.scale, rows=rows,
+                                     **O.zigzag_block_args(kind))
+            out, lse = (bo, bl) if out is None else O.merge(out, lse, bo, bl)[:2]
+        for s in range(cp):
+            src, kind = O.zigzag_step(r, s, cp)
+            O.block_backward(do, q, ks[src], vs[src], out, lse, cu_l, cu_l, case.scale, rows=rows,
+                             **O.zigzag_block_args(kind))
+        dt = time.perf_counter() - t0
+        pairs = 0
+        # visible pairs of the sampled rows per q head
+        for s in range(cp):
+            kind = O.zigzag_step(r, s, cp)[1]
+            a = O.zigzag_block_args(kind)
+            for d_, (qs, qe) in enumerate(O.doc_bounds(cu_l)):
+                qa, qb = O.view_range(qs, qe, a.get("q_view", "all"))
+                ka, kb = O.view_range(qs, qe, a.get("k_view", "all"))
+                sel = rows[(rows >= qa) & (rows < qb)]
+                if a.get("causal"):
+                    pairs += int(np.sum(np.minimum(sel - qs + 1, kb - ka)))
+                else:
+                    pairs += len(sel) * (kb - ka)
+        return dt, pairs
+
+    dt, _ = run(16)
+    n = int(min(2048, max(16, 16 * target_s / max(dt, 1e-3))))
+    dt, pairs = run(n)
+    hq, d = q.shape[1], q.shape[2]
+    flops = pairs * (4 + 10) * d * hq
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} sampled query rows of the headline rank (fwd 8 blocks + merges, bwd 8 blocks), "
+                      f"{pairs} visible pairs x 32 heads, {dt:.1f} s on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rows", choices=["all", "headline"], default="all")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the virtual-rank schedules run all ranks on a single device and "
+              "there is no multi-GPU path in this build (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from blockwise_causal_varlen_amd import inputs as I, lib, workloads as W
+    lib.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    h = headline(args, torch, lib, I, W)
+    log(f"headline: {h['ms_per_step']:.3f} ms/step, {h['value']:.1f} TFLOP/s fwd+bwd")
+    case = h.pop("case")
+    del h["wl"]
+    torch.cuda.empty_cache()
+    rows = other_rows(args, torch, lib, I, W) if args.rows == "all" else {}
+    for k, v in rows.items():
+        log(f"row {k}: {json.dumps({kk: vv for kk, vv in v.items() if kk != 'kernel_ms'})}")
+    cpu = cpu_baseline(case, args.cpu_seconds, np) if args.cpu_baseline == "on" else None
+    dom = h["kernels"][h["dominant"]]
+    line = {
+        "metric": METRIC,
+        "value": round(h["value"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": h["config"],
+        "roofline": {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")},
+        "cpu_baseline": cpu,
+        "fraction_of_bf16_peak": round(h["value"] / PEAK_BF16_TFLOPS, 4),
+        "kernels": h["kernels"],
+        "kernel_ms_total": {k: {"launches": v[0], "ms": round(v[1], 4)} for k, v in h["kernel_ms"].items()},
+        "rows": rows,
+        "sources": sources_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -42,6 +44,50 @@ attn_status hip_check(hipError_t e, const char *what) {
     attn_status _s = (x);             \
     if (_s != ATTN_OK) return _s;     \
   } while (0)
+
+// ---------------------------------------------------------------------------
+// Kernel timing: when enabled, each launch is bracketed by two hipEvents on
+// its stream; attn_timing_report reads and clears them.
+// ---------------------------------------------------------------------------
+struct Span {
+  const char *name;
+  hipEvent_t a, b;
+};
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<Span> spans;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<long, double>> agg;  // read but not yet delivered
+};
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+hipEvent_t pooled_event() {
+  Timing &t = timing();
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(const char *name, hipStream_t s, F &&launch) {
+  Timing &t = timing();
+  if (!t.on) return launch();
+  std::lock_guard<std::mutex> lk(t.mu);
+  Span sp{name, pooled_event(), pooled_event()};
+  if (sp.a) hipEventRecord(sp.a, s);
+  hipError_t e = launch();
+  if (sp.b) hipEventRecord(sp.b, s);
+  if (sp.a && sp.b) t.spans.push_back(sp);
+  return e;
+}
 
 int esize(int32_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
 
@@ -245,7 +291,7 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
     a.scale = scale; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
     a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
     a.lse = lse; a.lse_n = P.n_q; a.n_k = k->n_tok;
-    return hip_check(launch_decode(a, s), "decode kernel");
+    return hip_check(timed("attn_decode", s, [&] { return launch_decode(a, s); }), "decode kernel");
   }
 
   const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
@@ -253,8 +299,10 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
   SchedBufs sb = sched_carve(w, cap);
   w += align256(sched_bytes(cap));
   MaskDev md = mask_dev(mask);
-  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM, kFwdBN, 0,
-                                (int32_t)P.nseg, sb, s), "scheduler"));
+  TRY(hip_check(timed("attn_sched", s, [&] {
+                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM,
+                                         kFwdBN, 0, (int32_t)P.nseg, sb, s);
+                }), "scheduler"));
   FwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v);
   a.dtype = q->dtype; a.head_dim = (int32_t)P.d; a.hq = (int32_t)P.hq; a.hkv = (int32_t)P.hkv;
@@ -275,9 +323,10 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
     w += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
     a.part_lse = (float *)w;
     // segments no tile reaches must read as empty partials
-    TRY(hip_check(launch_fill(a.part_lse, P.nseg * P.hq * P.n_q, -INFINITY, s), "fill"));
+    TRY(hip_check(timed("attn_fill", s, [&] { return launch_fill(a.part_lse, P.nseg * P.hq * P.n_q, -INFINITY, s); }),
+                  "fill"));
   }
-  TRY(hip_check(launch_fwd(a, s), "forward kernel"));
+  TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd(a, s); }), "forward kernel"));
   if (P.nseg > 0) {
     MergeNArgs mn{};
     mn.n_parts = (int32_t)P.nseg;
@@ -288,7 +337,7 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
     mn.plse[0] = a.part_lse;
     mn.out = out->data; mn.out_dtype = out->dtype; mn.o_st = out->stride_tok; mn.o_sh = out->stride_head;
     mn.lse = lse; mn.n = P.n_q; mn.h = P.hq; mn.d = P.d;
-    TRY(hip_check(launch_merge_n(mn, s), "segment merge"));
+    TRY(hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(mn, s); }), "segment merge"));
   }
   return ok();
 }
@@ -321,7 +370,8 @@ attn_status attn_merge_out_lse(const attn_tensor *out, float *lse, const attn_te
   a.f_st = final_out ? final_out->stride_tok : 0; a.f_sh = final_out ? final_out->stride_head : 0;
   a.cu = cu_seqlens; a.num_seqs = num_seqs; a.view = (int32_t)q_view;
   a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim; a.init = init ? 1 : 0;
-  return hip_check(launch_merge(a, (hipStream_t)stream), "merge kernel");
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_merge", s, [&] { return launch_merge(a, s); }), "merge kernel");
 }
 
 attn_status attn_merge_n(int32_t n_parts, const attn_tensor *parts_out, const float *const *parts_lse,
@@ -343,7 +393,8 @@ attn_status attn_merge_n(int32_t n_parts, const attn_tensor *parts_out, const fl
   }
   a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
   a.lse = lse; a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim;
-  return hip_check(launch_merge_n(a, (hipStream_t)stream), "merge_n kernel");
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(a, s); }), "merge_n kernel");
 }
 
 attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
@@ -357,7 +408,8 @@ attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, floa
   a.dout = dout->data; a.dtype_do = dout->dtype; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
   a.out = out->data; a.dtype_o = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
   a.delta = delta; a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim;
-  return hip_check(launch_delta(a, (hipStream_t)stream), "delta kernel");
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_delta", s, [&] { return launch_delta(a, s); }), "delta kernel");
 }
 
 attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
@@ -413,10 +465,14 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
     delta = dl;
   }
   MaskDev md = mask_dev(mask);
-  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN, 0, 1,
-                                sq, s), "scheduler"));
-  TRY(hip_check(launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ, 1, 1,
-                                sk, s), "scheduler"));
+  TRY(hip_check(timed("attn_sched", s, [&] {
+                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN,
+                                         0, 1, sq, s);
+                }), "scheduler"));
+  TRY(hip_check(timed("attn_sched", s, [&] {
+                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ,
+                                         1, 1, sk, s);
+                }), "scheduler"));
   BwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v); a.dout = tdev(dout);
   a.dtype = q->dtype; a.head_dim = (int32_t)q->head_dim; a.hq = (int32_t)q->n_head; a.hkv = (int32_t)k->n_head;
@@ -425,7 +481,8 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   a.dk = (float *)dk->data; a.dk_st = dk->stride_tok; a.dk_sh = dk->stride_head;
   a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;
   a.qsched = sq; a.ksched = sk; a.q_items = capq; a.k_items = capk;
-  return hip_check(launch_bwd(a, s), "backward kernels");
+  TRY(hip_check(timed("attn_dkdv", s, [&] { return launch_bwd(a, 0, s); }), "dK/dV kernel"));
+  return hip_check(timed("attn_dq", s, [&] { return launch_bwd(a, 1, s); }), "dQ kernel");
 }
 
 attn_status attn_zigzag_shard(const attn_tensor *src, const int32_t *cu_seqlens_global, int32_t num_seqs,
@@ -439,10 +496,11 @@ attn_status attn_zigzag_shard(const attn_tensor *src, const int32_t *cu_seqlens_
   if (dst->n_tok * cp != src->n_tok) return fail(ATTN_ERR_SHAPE, "dst must hold n_src / cp rows");
   if (num_seqs < 0 || max_seqlen < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative sizes");
   if (num_seqs > 0 && !cu_seqlens_global) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
-  return hip_check(launch_zigzag_shard(src->data, src->stride_tok, src->stride_head, src->n_tok, dst->data,
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_zigzag_shard", s, [&] { return launch_zigzag_shard(src->data, src->stride_tok, src->stride_head, src->n_tok, dst->data,
                                        dst->stride_tok, dst->stride_head, dst->n_tok, esize(src->dtype),
                                        src->n_head, src->head_dim, cu_seqlens_global, num_seqs, max_seqlen, cp,
-                                       rank, (hipStream_t)stream),
+                                       rank, s); }),
                    "zigzag shard kernel");
 }
 
@@ -710,6 +768,47 @@ attn_status attn_validate_inputs(const attn_tensor *q, const attn_tensor *k, con
     const int64_t used = (ck[num_seqs] + mask->block_size - 1) / mask->block_size;
     for (int64_t b = 0; b < used && b < (int64_t)bt.size(); ++b)
       if (bt[b] < 0 || bt[b] >= pages) return fail(ATTN_ERR_CONTENT, "block_table[%lld] = %d out of range", (long long)b, bt[b]);
+  }
+  return ok();
+}
+
+attn_status attn_timing_enable(int32_t on) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return ok();
+}
+
+attn_status attn_timing_report(char *buf, size_t len, size_t *written) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  auto &agg = t.agg;
+  hipError_t err = hipSuccess;
+  for (const Span &sp : t.spans) {
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventSynchronize(sp.b);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, sp.a, sp.b);
+    auto &e = agg[sp.name];
+    e.first += 1;
+    e.second += ms;
+    t.pool.push_back(sp.a);
+    t.pool.push_back(sp.b);
+  }
+  t.spans.clear();
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "timing events: %s", hipGetErrorString(err));
+  std::string out;
+  char line[160];
+  for (auto &kv : agg) {
+    snprintf(line, sizeof line, "%s %ld %.6f\n", kv.first.c_str(), kv.second.first, kv.second.second);
+    out += line;
+  }
+  if (written) *written = out.size();
+  if (buf && len > 0) {
+    const size_t n = out.size() < len - 1 ? out.size() : len - 1;
+    memcpy(buf, out.data(), n);
+    buf[n] = 0;
+    if (out.size() >= len) return fail(ATTN_ERR_INVALID, "report needs %zu bytes", out.size() + 1);
+    agg.clear();  // delivered
   }
   return ok();
 }

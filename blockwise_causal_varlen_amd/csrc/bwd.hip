@@ -332,21 +332,22 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, hipStream_t s) {
-  BwdParams pk = base;
-  pk.items = a.ksched.items; pk.order = a.ksched.order; pk.count = a.ksched.count;
-  const int64_t gk = a.k_items * a.hkv;
-  if (gk > 0) hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  BwdParams pq = base;
-  pq.items = a.qsched.items; pq.order = a.qsched.order; pq.count = a.qsched.count;
-  const int64_t gq = a.q_items * a.hq;
-  if (gq > 0) hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pq);
+static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, int which, hipStream_t s) {
+  BwdParams pp = base;
+  if (which == 0) {
+    pp.items = a.ksched.items; pp.order = a.ksched.order; pp.count = a.ksched.count;
+    const int64_t gk = a.k_items * a.hkv;
+    if (gk > 0) hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+  } else {
+    pp.items = a.qsched.items; pp.order = a.qsched.order; pp.count = a.qsched.count;
+    const int64_t gq = a.q_items * a.hq;
+    if (gq > 0) hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
+// which = 0: the dK/dV kernel, 1: the dQ kernel.
+hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   BwdParams p;
   p.q = a.q.data; p.k = a.k.data; p.v = a.v.data; p.dout = a.dout.data;
   p.q_st = a.q.st; p.q_sh = a.q.sh; p.k_st = a.k.st; p.k_sh = a.k.sh;
@@ -359,11 +360,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   p.dk = a.dk; p.dk_st = a.dk_st; p.dk_sh = a.dk_sh;
   p.dv = a.dv; p.dv_st = a.dv_st; p.dv_sh = a.dv_sh;
   if (a.dtype == 0) {
-    if (a.head_dim == 128) return launch_bwd_t<bf16, 128>(p, a, s);
-    return launch_bwd_t<bf16, 64>(p, a, s);
+    if (a.head_dim == 128) return launch_bwd_t<bf16, 128>(p, a, which, s);
+    return launch_bwd_t<bf16, 64>(p, a, which, s);
   }
-  if (a.head_dim == 128) return launch_bwd_t<float, 128>(p, a, s);
-  return launch_bwd_t<float, 64>(p, a, s);
+  if (a.head_dim == 128) return launch_bwd_t<float, 128>(p, a, which, s);
+  return launch_bwd_t<float, 64>(p, a, which, s);
 }
 
 }  // namespace attn

@@ -75,21 +75,89 @@ __device__ __forceinline__ int64_t clampi(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
+// Block-wide inclusive scan of one int per thread (kSchedThreads threads).
+__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t *buf) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int32_t x = tid >= off ? buf[tid - off] : 0;
+    __syncthreads();
+    buf[tid] += x;
+    __syncthreads();
+  }
+  const int32_t r = buf[tid];
+  __syncthreads();
+  return r;
+}
+
+__device__ void make_item(const SchedParams &p, int64_t qs, int64_t qe, int64_t ks, int64_t ke, int64_t t,
+                          int64_t sg, WorkItem &it) {
+  const MaskDev &m = p.m;
+  int64_t qa, qb, ka, kb;
+  view_range(qs, qe, m.q_view, qa, qb);
+  view_range(ks, ke, m.k_view, ka, kb);
+  const int64_t nk_doc = ke - ks;
+  it.qdoc0 = (int32_t)qs;
+  it.kdoc0 = (int32_t)ks;
+  it.seg = (int32_t)sg;
+  if (p.by_keys) {
+    // a tile of keys and the query rows that can see any of them
+    const int64_t k0 = ka + t * p.tile;
+    const int64_t k1 = k0 + p.tile < kb ? k0 + p.tile : kb;
+    int64_t lo = qa, hi = qb;
+    if (m.causal) {  // qpos >= kpos(first key)
+      const int64_t c = qs + (m.pm.kpos(k0 - ks) - m.q_pos_offset);
+      if (c > lo) lo = c;
+    }
+    if (m.window > 0) {  // qpos < kpos(last key) + window
+      const int64_t c = qs + (m.pm.kpos(k1 - 1 - ks) + m.window - m.q_pos_offset);
+      if (c < hi) hi = c;
+    }
+    if (hi < lo) hi = lo;
+    it.q0 = (int32_t)lo; it.q1 = (int32_t)hi;
+    it.k0 = (int32_t)k0; it.k1 = (int32_t)k1;
+    it.cost = (int32_t)((hi - lo + p.key_tile - 1) / p.key_tile + 1);
+    return;
+  }
+  const int64_t q0 = qa + t * p.tile;
+  const int64_t q1 = q0 + p.tile < qb ? q0 + p.tile : qb;
+  // keys any row of the tile can see
+  int64_t lo = ka, hi = kb;
+  if (m.causal) {
+    const int64_t c = ks + m.pm.count_le(m.q_pos_offset + (q1 - 1 - qs), nk_doc);
+    if (c < hi) hi = c;
+  }
+  if (m.window > 0) {
+    const int64_t c = ks + m.pm.count_le(m.q_pos_offset + (q0 - qs) - m.window, nk_doc);
+    if (c > lo) lo = c;
+  }
+  if (m.seg_size > 0) {
+    const int64_t sa = ks + sg * m.seg_size, sbd = sa + m.seg_size;
+    if (sa > lo) lo = sa;
+    if (sbd < hi) hi = sbd;
+  }
+  if (hi < lo) hi = lo;
+  it.q0 = (int32_t)q0; it.q1 = (int32_t)q1;
+  it.k0 = (int32_t)lo; it.k1 = (int32_t)hi;
+  it.cost = (int32_t)((hi - lo + p.key_tile - 1) / p.key_tile + 1);
+}
+
 __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
-  __shared__ int32_t s_scan[kSchedThreads];
+  __shared__ int32_t s_buf[kSchedThreads];
+  __shared__ int32_t s_base[kSchedThreads + 1];  // first item of each doc in the chunk
+  __shared__ int32_t s_nseg[kSchedThreads];
   __shared__ int32_t s_hist[kCostBins];
-  __shared__ int32_t s_total;
   const int tid = threadIdx.x;
   const MaskDev &m = p.m;
   int64_t running = 0;
   for (int c0 = 0; c0 < p.num_seqs; c0 += kSchedThreads) {
     const int d = c0 + tid;
-    int64_t qs = 0, qe = 0, ks = 0, ke = 0, qa = 0, qb = 0, ka = 0, kb = 0, nseg = 1, ntile = 0;
+    int64_t ntile = 0, nseg = 1;
     if (d < p.num_seqs) {
-      qs = clampi(p.cu_q[d], 0, p.n_q);
-      qe = clampi(p.cu_q[d + 1], qs, p.n_q);
-      ks = clampi(p.cu_k[d], 0, p.n_k);
-      ke = clampi(p.cu_k[d + 1], ks, p.n_k);
+      const int64_t qs = clampi(p.cu_q[d], 0, p.n_q), qe = clampi(p.cu_q[d + 1], qs, p.n_q);
+      const int64_t ks = clampi(p.cu_k[d], 0, p.n_k), ke = clampi(p.cu_k[d + 1], ks, p.n_k);
+      int64_t qa, qb, ka, kb;
       view_range(qs, qe, m.q_view, qa, qb);
       view_range(ks, ke, m.k_view, ka, kb);
       ntile = p.by_keys ? (kb - ka + p.tile - 1) / p.tile : (qb - qa + p.tile - 1) / p.tile;
@@ -97,86 +165,36 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
       if (nseg > p.max_seg) nseg = p.max_seg;
       if (nseg < 1) nseg = 1;
     }
-    int32_t mine = (int32_t)(ntile * nseg);
-    // block exclusive scan
-    s_scan[tid] = mine;
+    const int32_t mine = (int32_t)(ntile * nseg);
+    const int32_t incl = block_scan(mine, s_buf);
+    s_base[tid] = incl - mine;
+    s_nseg[tid] = (int32_t)nseg;
+    if (tid == kSchedThreads - 1) s_base[kSchedThreads] = incl;
     __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-      int32_t v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    int64_t base = running + s_scan[tid] - mine;
-    if (tid == kSchedThreads - 1) s_total = s_scan[tid];
-    __syncthreads();
-    running += s_total;
-    __syncthreads();
-    if (d < p.num_seqs) {
-      const int64_t nk_doc = ke - ks;
-      for (int64_t t = 0; p.by_keys && t < ntile; ++t) {
-        // a tile of keys and the query rows that can see any of them
-        const int64_t k0 = ka + t * p.tile;
-        const int64_t k1 = k0 + p.tile < kb ? k0 + p.tile : kb;
-        int64_t lo = qa, hi = qb;
-        if (m.causal) {  // qpos >= kpos(first key)
-          const int64_t c = qs + (m.pm.kpos(k0 - ks) - m.q_pos_offset);
-          if (c > lo) lo = c;
-        }
-        if (m.window > 0) {  // qpos < kpos(last key) + window
-          const int64_t c = qs + (m.pm.kpos(k1 - 1 - ks) + m.window - m.q_pos_offset);
-          if (c < hi) hi = c;
-        }
-        if (hi < lo) hi = lo;
-        const int64_t idx = base + t;
-        if (idx >= p.sb.capacity) continue;
-        WorkItem it;
-        it.q0 = (int32_t)lo; it.q1 = (int32_t)hi;
-        it.k0 = (int32_t)k0; it.k1 = (int32_t)k1;
-        it.qdoc0 = (int32_t)qs; it.kdoc0 = (int32_t)ks;
-        it.seg = 0;
-        it.cost = (int32_t)((hi - lo + p.key_tile - 1) / p.key_tile + 1);
-        p.sb.items[idx] = it;
+    const int32_t chunk_total = s_base[kSchedThreads];
+    // one thread per item: find its document by binary search over s_base
+    for (int32_t i = tid; i < chunk_total; i += kSchedThreads) {
+      int lo = 0, hi = kSchedThreads;  // s_base[lo] <= i < s_base[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_base[mid] <= i) lo = mid; else hi = mid;
       }
-      for (int64_t t = 0; !p.by_keys && t < ntile; ++t) {
-        const int64_t q0 = qa + t * p.tile;
-        const int64_t q1 = q0 + p.tile < qb ? q0 + p.tile : qb;
-        // keys any row of the tile can see
-        int64_t lo = ka, hi = kb;
-        if (m.causal) {
-          const int64_t pmax = m.q_pos_offset + (q1 - 1 - qs);
-          const int64_t c = ks + m.pm.count_le(pmax, nk_doc);
-          if (c < hi) hi = c;
-        }
-        if (m.window > 0) {
-          const int64_t pmin = m.q_pos_offset + (q0 - qs);
-          const int64_t c = ks + m.pm.count_le(pmin - m.window, nk_doc);
-          if (c > lo) lo = c;
-        }
-        for (int64_t sg = 0; sg < nseg; ++sg) {
-          const int64_t idx = base + t * nseg + sg;
-          if (idx >= p.sb.capacity) continue;
-          int64_t a = lo, b = hi;
-          if (m.seg_size > 0) {
-            const int64_t sa = ks + sg * m.seg_size, sbd = sa + m.seg_size;
-            if (sa > a) a = sa;
-            if (sbd < b) b = sbd;
-          }
-          if (b < a) b = a;
-          WorkItem it;
-          it.q0 = (int32_t)q0; it.q1 = (int32_t)q1;
-          it.k0 = (int32_t)a; it.k1 = (int32_t)b;
-          it.qdoc0 = (int32_t)qs; it.kdoc0 = (int32_t)ks;
-          it.seg = (int32_t)sg;
-          it.cost = (int32_t)((b - a + p.key_tile - 1) / p.key_tile + 1);
-          p.sb.items[idx] = it;
-        }
-      }
+      const int64_t idx = running + i;
+      if (idx >= p.sb.capacity) continue;
+      const int dd = c0 + lo;
+      const int32_t local = i - s_base[lo];
+      const int32_t ns = s_nseg[lo];
+      const int64_t qs = clampi(p.cu_q[dd], 0, p.n_q), qe = clampi(p.cu_q[dd + 1], qs, p.n_q);
+      const int64_t ks = clampi(p.cu_k[dd], 0, p.n_k), ke = clampi(p.cu_k[dd + 1], ks, p.n_k);
+      WorkItem it;
+      make_item(p, qs, qe, ks, ke, local / ns, local % ns, it);
+      p.sb.items[idx] = it;
     }
+    running += chunk_total;
     __syncthreads();
   }
   const int32_t count = (int32_t)(running < p.sb.capacity ? running : p.sb.capacity);
-  // counting sort by decreasing cost
+  // counting sort by decreasing cost (bin kCostBins-1-cost)
   for (int i = tid; i < kCostBins; i += kSchedThreads) s_hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < count; i += kSchedThreads) {
@@ -185,19 +203,19 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
     atomicAdd(&s_hist[kCostBins - 1 - c], 1);
   }
   __syncthreads();
-  if (tid == 0) {  // exclusive scan over bins (2048 entries, once per launch)
-    int32_t acc = 0;
-    for (int i = 0; i < kCostBins; ++i) {
-      int32_t v = s_hist[i];
-      s_hist[i] = acc;
-      acc += v;
-    }
-  }
+  constexpr int BPT = kCostBins / kSchedThreads;  // bins per thread
+  int32_t loc[BPT], sum = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) { loc[j] = s_hist[tid * BPT + j]; sum += loc[j]; }
+  const int32_t incl = block_scan(sum, s_buf);
+  int32_t acc = incl - sum;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) { s_hist[tid * BPT + j] = acc; acc += loc[j]; }
   __syncthreads();
   for (int i = tid; i < count; i += kSchedThreads) {
     int c = p.sb.items[i].cost;
     c = c >= kCostBins ? kCostBins - 1 : c;
-    int pos = atomicAdd(&s_hist[kCostBins - 1 - c], 1);
+    const int pos = atomicAdd(&s_hist[kCostBins - 1 - c], 1);
     p.sb.order[pos] = i;
   }
   if (tid == 0) *p.sb.count = count;

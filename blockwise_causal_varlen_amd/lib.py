@@ -76,6 +76,8 @@ _SIGS = {
     "attn_kvp_workspace_size": (C.c_int, [I32, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
     "attn_kvp_fwd": (C.c_int, [I32, T, T, T, C.POINTER(P), P, P, I32, I32, I32, M, F, T, P, P, SZ, P]),
     "attn_validate_inputs": (C.c_int, [T, T, P, P, I32, I32, I32, M, I32, I32, P]),
+    "attn_timing_enable": (C.c_int, [I32]),
+    "attn_timing_report": (C.c_int, [C.c_char_p, SZ, C.POINTER(SZ)]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -376,3 +378,20 @@ def validate_inputs(q, k, cu_q, cu_k, max_q, max_k, m=None, zigzag_cp=0, one_que
     kd = k_desc or desc(k)
     _call("attn_validate_inputs", C.byref(desc(q)), C.byref(kd), cq.data_ptr(), ck.data_ptr(), cq.numel() - 1, max_q,
           max_k, _ref(m), zigzag_cp, one_query, _stream(stream))
+
+
+def attn_timing_enable(on: bool):
+    _call("attn_timing_enable", int(bool(on)))
+
+
+def attn_timing_report() -> dict:
+    """{kernel name: (launches, total ms)} since the last report (waits for the events)."""
+    n = SZ(0)
+    _call("attn_timing_report", None, 0, C.byref(n))
+    buf = C.create_string_buffer(n.value + 1)
+    _call("attn_timing_report", buf, n.value + 1, C.byref(n))
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out

@@ -364,6 +364,20 @@ attn_status attn_validate_inputs(const attn_tensor *q, const attn_tensor *k,
                                  const attn_mask *mask, int32_t zigzag_cp, int32_t one_query,
                                  void *stream);
 
+/*
+ * Kernel timing (tracing). With timing enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on the launch stream (the
+ * events come from a pool the library keeps for the process; no device
+ * memory is allocated). attn_timing_report waits for the recorded events and
+ * writes one line per kernel, "name launches total_ms\n", into buf (len bytes
+ * including the terminating 0; *written = bytes needed without it), then
+ * clears the record; with buf == NULL (a size query) or a buffer that is too
+ * small the record is kept. Not for use under graph capture. Process-wide
+ * and thread-safe; spans of concurrent callers are merged.
+ */
+attn_status attn_timing_enable(int32_t on);
+attn_status attn_timing_report(char *buf, size_t len, size_t *written);
+
 #ifdef __cplusplus
 }
 #endif
