@@ -51,6 +51,9 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    for f in os.listdir(BUILD):  # never link a stale object
+        if f.endswith(".o"):
+            os.remove(os.path.join(BUILD, f))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
@@ -62,5 +65,15 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def main(argv) -> int:
+    try:
+        path = build(verbose="-v" in argv)
+    except RuntimeError as e:
+        print(f"BUILD FAILED: {e}", file=sys.stderr)
+        return 1
+    print(path)
+    return 0
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    sys.exit(main(sys.argv))

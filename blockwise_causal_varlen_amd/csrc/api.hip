@@ -208,6 +208,7 @@ size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs) {
 size_t bwd_ws_bytes(int64_t n_q, int64_t n_k, int64_t hq, int32_t num_seqs, bool need_delta) {
   size_t b = align256(sched_bytes(sched_capacity(n_q, num_seqs, kBwdTile, 1)));
   b += align256(sched_bytes(sched_capacity(n_k, num_seqs, kBwdTile, 1)));
+  b += align256((size_t)hq * n_q * 4);  // lse in log2 units
   if (need_delta) b += align256((size_t)hq * n_q * 4);
   return b;
 }
@@ -459,6 +460,9 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   w += align256(sched_bytes(capq));
   SchedBufs sk = sched_carve(w, capk);
   w += align256(sched_bytes(capk));
+  float *lse2 = (float *)w;
+  w += align256((size_t)q->n_head * q->n_tok * 4);
+  TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, s); }), "lse2"));
   if (!delta) {
     float *dl = (float *)w;
     TRY(attn_bwd_delta(dout, out, dl, stream));
@@ -476,7 +480,7 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   BwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v); a.dout = tdev(dout);
   a.dtype = q->dtype; a.head_dim = (int32_t)q->head_dim; a.hq = (int32_t)q->n_head; a.hkv = (int32_t)k->n_head;
-  a.scale = scale; a.mask = md; a.lse = lse; a.delta = delta; a.n_q = q->n_tok; a.n_k = k->n_tok;
+  a.scale = scale; a.mask = md; a.lse = lse; a.delta = delta; a.lse2 = lse2; a.n_q = q->n_tok; a.n_k = k->n_tok;
   a.dq = (float *)dq->data; a.dq_st = dq->stride_tok; a.dq_sh = dq->stride_head;
   a.dk = (float *)dk->data; a.dk_st = dk->stride_tok; a.dk_sh = dk->stride_head;
   a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;

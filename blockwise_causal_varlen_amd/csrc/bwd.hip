@@ -38,6 +38,7 @@ struct BwdParams {
   float scale, scale_log2;
   MaskDev m;
   const float *lse, *delta;
+  const float *lse2;  // lse * log2(e), +inf where lse = -inf (rows that see nothing)
   int64_t n_q;
   float *dq; int64_t dq_st, dq_sh;
   float *dk; int64_t dk_st, dk_sh;
@@ -307,11 +308,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
       const int32_t t0 = (int32_t)(kt - it.kdoc0);
       const int32_t nvalid = (int32_t)(it.k1 - kt);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int32_t kk = sb * 32 + c_row(j, lane);
-        const bool vis = full | ((kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window));
-        const float e = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -lrow));
-        ds[j] = vis ? e * (dp[j] - drow) : 0.f;
+      for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -lrow)) * (dp[j] - drow);
+      if (!full) {  // wave-uniform
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t kk = sb * 32 + c_row(j, lane);
+          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
+          ds[j] = vis ? ds[j] : 0.f;
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<T>(dq[dt], sK, PK, sb * 32, dt, ds, lane);
@@ -331,17 +335,297 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernels with asynchronous double-buffered staging (global->LDS copies
+// through buffer resources; rows past the end of a tile read as zeros, which
+// contribute nothing: zero q/dout rows give dS = 0 and P^T dout = 0).
+// ---------------------------------------------------------------------------
+__global__ void lse2_kernel(const float *lse, float *lse2, int64_t n) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float l = lse[i];
+    lse2[i] = l == neg_inf() ? __builtin_inff() : l * kLog2e;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
+  using M = Mfma32<bf16>;
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int QB = kBwdBQ;
+  static_assert(QB == 64, "tiles are 64 rows");
+  using QT = PadTile<D, D / 8 + 5>;  // row reads and transpose reads
+  __shared__ __attribute__((aligned(1024))) bf16 sQ0[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sO0[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sQ1[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sO1[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) float sL0[QB];
+  __shared__ __attribute__((aligned(16))) float sD0[QB];
+  __shared__ __attribute__((aligned(16))) float sL1[QB];
+  __shared__ __attribute__((aligned(16))) float sD1[QB];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hkv_count = p.hq / p.group;
+  const int rank = blockIdx.x / hkv_count;
+  const int hk = blockIdx.x - rank * hkv_count;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const MaskDev &m = p.m;
+
+  const int64_t kr0 = it.k0 + 32 * w;
+  const int64_t key = kr0 + l32;
+  const bool key_ok = key < it.k1;
+  const bool wave_on = kr0 < it.k1;
+  const int64_t kp_lane = m.pm.kpos(key - it.kdoc0);
+  const int64_t wk_lo = m.pm.kpos(kr0 - it.kdoc0);
+  const int64_t wk_hi = m.pm.kpos((kr0 + 31 < it.k1 ? kr0 + 31 : it.k1 - 1) - it.kdoc0);
+
+  bf16x8 kf[NS], vf[NS];
+  {
+    const bf16 *krow = (const bf16 *)p.k + key * p.k_st + (int64_t)hk * p.k_sh;
+    const bf16 *vrow = (const bf16 *)p.v + key * p.v_st + (int64_t)hk * p.v_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = glob_row_frag<bf16>(krow, s, g, key_ok);
+      vf[s] = glob_row_frag<bf16>(vrow, s, g, key_ok);
+    }
+  }
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
+
+  int qoff[QT::NJ], ooff[QT::NJ];
+  tile_voffsets<QT>(qoff, p.q_st, w, lane);
+  tile_voffsets<QT>(ooff, p.do_st, w, lane);
+  const int nqt = (int)((it.q1 - it.q0 + QB - 1) / QB);
+  const int total = p.group * nqt;
+  const bf16 *qb = (const bf16 *)p.q;
+  const bf16 *ob = (const bf16 *)p.dout;
+
+  auto stage = [&](bf16 *sq, bf16 *so, float *sl, float *sd, int i) {
+    const int hh = i / nqt;
+    const int64_t qt = it.q0 + (int64_t)(i - hh * nqt) * QB;
+    const int h = hk * p.group + hh;
+    const int nvalid = (int)(it.q1 - qt < QB ? it.q1 - qt : QB);
+    dma_tile_buf<QT>(sq, qb + qt * p.q_st + (int64_t)h * p.q_sh, tile_bytes(p.q_st, nvalid, D), qoff, w);
+    dma_tile_buf<QT>(so, ob + qt * p.do_st + (int64_t)h * p.do_sh, tile_bytes(p.do_st, nvalid, D), ooff, w);
+    if (w < 2) {
+      const float *src = (w == 0 ? p.lse2 : p.delta) + (int64_t)h * p.n_q + qt;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nvalid * 4, kBufFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(w == 0 ? sl : sd), 4, lane * 4, 0, 0, 0);
+    }
+  };
+
+  auto compute = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd, int i) {
+    if (!wave_on) return;
+    const int hh = i / nqt;
+    const int64_t qt = it.q0 + (int64_t)(i - hh * nqt) * QB;
+#pragma unroll
+    for (int sub = 0; sub < QB / 32; ++sub) {
+      const int64_t qs0 = qt + sub * 32;
+      if (qs0 >= it.q1) break;
+      const int64_t qlast = (qs0 + 31 < it.q1 ? qs0 + 31 : it.q1 - 1);
+      const int64_t qp_lo = m.q_pos_offset + (qs0 - it.qdoc0);
+      const int64_t qp_hi = m.q_pos_offset + (qlast - it.qdoc0);
+      if (m.causal && wk_lo > qp_hi) continue;
+      if (m.window > 0 && wk_hi <= qp_lo - m.window) continue;
+      const bool full = (!m.causal || wk_hi <= qp_lo) && (m.window <= 0 || wk_lo > qp_hi - m.window);
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const int off = (sub * 32 + l32) * QT::PITCH + st * 16 + g * 8;
+        s = M::mma(*reinterpret_cast<const bf16x8 *>(sq + off), kf[st], s);
+        dp = M::mma(*reinterpret_cast<const bf16x8 *>(so + off), vf[st], dp);
+      }
+      float pv[16], ds[16];
+      const int64_t qp0 = m.q_pos_offset + (qt - it.qdoc0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int q4 = sub * 32 + 8 * a + 4 * g;  // rows c_row(4a..4a+3)
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + q4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sd + q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * a + e;
+          const bool vis = full | visible(qp0 + q4 + e, kp_lane, m.causal, m.window);
+          const float ex = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -l4[e]));
+          pv[j] = vis ? ex : 0.f;
+          ds[j] = pv[j] * (dp[j] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        dv[dt] = acc_transposed<bf16>(dv[dt], so, QT::PITCH, sub * 32, dt, pv, lane);
+        dk[dt] = acc_transposed<bf16>(dk[dt], sq, QT::PITCH, sub * 32, dt, ds, lane);
+      }
+    }
+  };
+
+  if (total > 0) stage(sQ0, sO0, sL0, sD0, 0);
+  __syncthreads();
+  for (int i = 0; i < total; i += 2) {
+    if (i + 1 < total) stage(sQ1, sO1, sL1, sD1, i + 1);
+    compute(sQ0, sO0, sL0, sD0, i);
+    __syncthreads();
+    if (i + 1 >= total) break;
+    if (i + 2 < total) stage(sQ0, sO0, sL0, sD0, i + 2);
+    compute(sQ1, sO1, sL1, sD1, i + 1);
+    __syncthreads();
+  }
+  if (!key_ok) return;
+  float *dkr = p.dk + key * p.dk_st + (int64_t)hk * p.dk_sh;
+  float *dvr = p.dv + key * p.dv_st + (int64_t)hk * p.dv_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      float4 a = *reinterpret_cast<float4 *>(dkr + d0);
+      a.x += p.scale * dk[dt][4 * j4]; a.y += p.scale * dk[dt][4 * j4 + 1];
+      a.z += p.scale * dk[dt][4 * j4 + 2]; a.w += p.scale * dk[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dkr + d0) = a;
+      float4 b = *reinterpret_cast<float4 *>(dvr + d0);
+      b.x += dv[dt][4 * j4]; b.y += dv[dt][4 * j4 + 1]; b.z += dv[dt][4 * j4 + 2]; b.w += dv[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dvr + d0) = b;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams p) {
+  using M = Mfma32<bf16>;
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int KB = kFwdBN;
+  static_assert(KB == 64, "tiles are 64 rows");
+  using KT = PadTile<D, D / 8 + 5>;  // row reads and transpose reads
+  using VT = PadTile<D, D / 8 + 1>;  // row reads
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[KT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[VT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[KT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[VT::ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rank = blockIdx.x / p.hq;
+  const int h = blockIdx.x - rank * p.hq;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const int hk = h / p.group;
+  const MaskDev &m = p.m;
+
+  const int64_t r0 = it.q0 + 32 * w;
+  const int64_t row = r0 + l32;
+  const bool row_ok = row < it.q1;
+  const bool wave_on = r0 < it.q1;
+  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
+  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
+  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+
+  bf16x8 qf[NS], of[NS];
+  {
+    const bf16 *qrow = (const bf16 *)p.q + row * p.q_st + (int64_t)h * p.q_sh;
+    const bf16 *orow = (const bf16 *)p.dout + row * p.do_st + (int64_t)h * p.do_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = glob_row_frag<bf16>(qrow, s, g, row_ok);
+      of[s] = glob_row_frag<bf16>(orow, s, g, row_ok);
+    }
+  }
+  const float lrow = row_ok ? p.lse2[(int64_t)h * p.n_q + row] : __builtin_inff();
+  const float drow = row_ok ? p.delta[(int64_t)h * p.n_q + row] : 0.f;
+  f32x16 dq[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) dq[i] = f32x16{};
+
+  int koff[KT::NJ], voff[VT::NJ];
+  tile_voffsets<KT>(koff, p.k_st, w, lane);
+  tile_voffsets<VT>(voff, p.v_st, w, lane);
+  const bf16 *kb = (const bf16 *)p.k;
+  const bf16 *vb = (const bf16 *)p.v;
+  auto stage = [&](bf16 *sk, bf16 *sv, int64_t kt) {
+    const int nvalid = (int)(it.k1 - kt < KB ? it.k1 - kt : KB);
+    dma_tile_buf<KT>(sk, kb + kt * p.k_st + (int64_t)hk * p.k_sh, tile_bytes(p.k_st, nvalid, D), koff, w);
+    dma_tile_buf<VT>(sv, vb + kt * p.v_st + (int64_t)hk * p.v_sh, tile_bytes(p.v_st, nvalid, D), voff, w);
+  };
+  auto compute = [&](const bf16 *sk, const bf16 *sv, int64_t kt) {
+    if (!wave_on) return;
+    const int64_t klast = (kt + KB <= it.k1 ? kt + KB : it.k1) - 1;
+    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
+    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
+    if (m.causal && kp_lo > wq_hi) return;
+    if (m.window > 0 && kp_hi <= wq_lo - m.window) return;
+    const bool full = (kt + KB <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
+                      (m.window <= 0 || kp_lo > wq_hi - m.window);
+    const int32_t t0 = (int32_t)(kt - it.kdoc0);
+    const int32_t nvalid = (int32_t)(it.k1 - kt);
+#pragma unroll
+    for (int sb = 0; sb < KB / 32; ++sb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        s = M::mma(*reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8), qf[st], s);
+        dp = M::mma(*reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8), of[st], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -lrow)) * (dp[j] - drow);
+      if (!full) {  // wave-uniform
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t kk = sb * 32 + c_row(j, lane);
+          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
+          ds[j] = vis ? ds[j] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<bf16>(dq[dt], sk, KT::PITCH, sb * 32, dt, ds, lane);
+    }
+  };
+
+  if (it.k0 < it.k1) stage(sK0, sV0, it.k0);
+  __syncthreads();
+  for (int64_t kt = it.k0; kt < it.k1; kt += 2 * KB) {
+    if (kt + KB < it.k1) stage(sK1, sV1, kt + KB);
+    compute(sK0, sV0, kt);
+    __syncthreads();
+    if (kt + KB >= it.k1) break;
+    if (kt + 2 * KB < it.k1) stage(sK0, sV0, kt + 2 * KB);
+    compute(sK1, sV1, kt + KB);
+    __syncthreads();
+  }
+  if (!row_ok) return;
+  float *dqr = p.dq + row * p.dq_st + (int64_t)h * p.dq_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      float4 a = *reinterpret_cast<float4 *>(dqr + d0);
+      a.x += p.scale * dq[dt][4 * j4]; a.y += p.scale * dq[dt][4 * j4 + 1];
+      a.z += p.scale * dq[dt][4 * j4 + 2]; a.w += p.scale * dq[dt][4 * j4 + 3];
+      *reinterpret_cast<float4 *>(dqr + d0) = a;
+    }
+}
+
 template <typename T, int D>
 static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, int which, hipStream_t s) {
   BwdParams pp = base;
+  constexpr bool kBf16 = sizeof(T) == 2;
   if (which == 0) {
     pp.items = a.ksched.items; pp.order = a.ksched.order; pp.count = a.ksched.count;
     const int64_t gk = a.k_items * a.hkv;
-    if (gk > 0) hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+    if (gk > 0) {
+      if constexpr (kBf16) hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+      else hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+    }
   } else {
     pp.items = a.qsched.items; pp.order = a.qsched.order; pp.count = a.qsched.count;
     const int64_t gq = a.q_items * a.hq;
-    if (gq > 0) hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+    if (gq > 0) {
+      if constexpr (kBf16) hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+      else hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+    }
   }
   return hipGetLastError();
 }
@@ -355,7 +639,7 @@ hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   p.hq = a.hq; p.group = a.hq / a.hkv;
   p.scale = a.scale; p.scale_log2 = a.scale * kLog2e;
   p.m = a.mask;
-  p.lse = a.lse; p.delta = a.delta; p.n_q = a.n_q;
+  p.lse = a.lse; p.delta = a.delta; p.lse2 = a.lse2; p.n_q = a.n_q;
   p.dq = a.dq; p.dq_st = a.dq_st; p.dq_sh = a.dq_sh;
   p.dk = a.dk; p.dk_st = a.dk_st; p.dk_sh = a.dk_sh;
   p.dv = a.dv; p.dv_st = a.dv_st; p.dv_sh = a.dv_sh;
@@ -365,6 +649,14 @@ hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   }
   if (a.head_dim == 128) return launch_bwd_t<float, 128>(p, a, which, s);
   return launch_bwd_t<float, 64>(p, a, which, s);
+}
+
+hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t b = (n + 255) / 256;
+  if (b > 8192) b = 8192;
+  hipLaunchKernelGGL(lse2_kernel, dim3((unsigned)b), dim3(256), 0, s, lse, lse2, n);
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -90,10 +90,9 @@ struct PosMap {
   // Branch-free 32-bit form for per-element masks (t, positions < 2^31 within
   // one document's window of interest; the offset is applied in 64 bits).
   __device__ __forceinline__ int64_t kpos32(int32_t t) const {
-    const int32_t bs = interleave ? block : 1;  // no division by zero when contiguous
-    const int32_t b = t / bs;
-    const int32_t rr = interleave ? ((b * interleave + rank) * bs + (t - b * bs)) : t;
-    return k_pos_offset + rr;
+    if (interleave == 0) return k_pos_offset + t;  // uniform branch
+    const int32_t b = t / block;
+    return k_pos_offset + ((b * interleave + rank) * block + (t - b * block));
   }
   // Number of keys t in [0, n) with kpos(t) <= p (monotone inverse).
   __device__ __forceinline__ int64_t count_le(int64_t p, int64_t n) const {
@@ -105,6 +104,87 @@ struct PosMap {
     return lo;
   }
 };
+
+// ---------------------------------------------------------------------------
+// Padded bf16 LDS tiles of 64 rows filled by direct global->LDS copies.
+// A row is PCH 16-byte chunks: D/8 data chunks + padding. The pitches used:
+//   D/8 + 1 chunks: 16-byte row reads of 16 rows hit 16 distinct bank groups;
+//   D/8 + 4 chunks: 4-row transpose reads of 64 bytes hit distinct banks;
+//   D/8 + 5 chunks: both patterns, the transpose reads at most 2-way.
+// A copy instruction moves 64 consecutive 16-byte slots (lane l -> slot
+// base + l), so slot s is (row s / PCH, chunk s % PCH); pad slots are given an
+// offset past the buffer range and read as zeros.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int PCH> struct PadTile {
+  static constexpr int CPR = D / 8;            // data chunks per row
+  static constexpr int NBLK = PCH;             // 1 KB blocks (64 rows x PCH chunks / 64)
+  static constexpr int NJ = (NBLK + 3) / 4;    // blocks per wave (4 waves)
+  static constexpr int PITCH = PCH * 8;        // elements per row
+  static constexpr int ELEMS = 64 * PITCH;     // elements per tile
+};
+
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kPastEnd = 0x40000000;   // a byte offset beyond any tile resource
+
+// Bytes of a tile resource covering its valid rows (rows past the end read 0).
+__device__ __forceinline__ int tile_bytes(int64_t st, int nvalid, int d) {
+  return nvalid > 0 ? (int)(((int64_t)(nvalid - 1) * st + d) * 2) : 0;
+}
+
+// Per-lane byte offsets (inside a tile, row stride st elements) of this
+// wave's copy instructions.
+template <class TT>
+__device__ __forceinline__ void tile_voffsets(int *voff, int64_t st, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < TT::NJ; ++j) {
+    const int blk = wave + 4 * j;
+    const int s = blk * 64 + lane;
+    const int r = s / TT::NBLK, c = s % TT::NBLK;
+    voff[j] = (blk < TT::NBLK && c < TT::CPR) ? (int)(r * st * 2) + c * 16 : kPastEnd;
+  }
+}
+
+// Asynchronous tile copy through a buffer resource; completion is awaited by
+// the next __syncthreads().
+template <class TT>
+__device__ __forceinline__ void dma_tile_buf(bf16 *lds, const bf16 *tile_row0, int bytes, const int *voff, int wave) {
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)tile_row0, (short)0, bytes, kBufFlags);
+#pragma unroll
+  for (int j = 0; j < TT::NJ; ++j) {
+    const int blk = wave + 4 * j;
+    if (blk < TT::NBLK)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16,
+                                               voff[j], 0, 0, 0);
+  }
+}
+
+// Asynchronous tile copy from per-row global addresses (paged keys).
+// row_ptr(r) must return a valid address for every r in [0, 64).
+template <class TT, typename RowPtr>
+__device__ __forceinline__ void dma_tile_rows(bf16 *lds, RowPtr row_ptr, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < TT::NJ; ++j) {
+    const int blk = wave + 4 * j;
+    if (blk < TT::NBLK) {
+      const int s = blk * 64 + lane;
+      const int r = s / TT::NBLK, c = s % TT::NBLK;
+      const bf16 *src = c < TT::CPR ? row_ptr(r) + c * 8 : row_ptr(0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Transpose read of a padded tile (pitch in elements): the lane's 16-lane
+// group u = lane % 16 supplies row r0 + u/4, columns col0 + 4*(u%4)..+3, and
+// receives rows r0..r0+3 of column col0 + u.
+__device__ __forceinline__ bf16x4 tile_tr4(const bf16 *t, int pitch, int r0, int col0, int u) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+  const bf16 *a = t + (r0 + (u >> 2)) * pitch + col0 + 4 * (u & 3);
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)a);
+  return __builtin_bit_cast(bf16x4, v);
+}
 
 // Visibility of (query position qp, key position kp) under causal / window,
 // written with bitwise ops so it compiles to selects, not branches.

@@ -495,12 +495,231 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward: K/V tiles arrive by asynchronous global->LDS copies into two
+// swizzled buffers, so tile t+1 is in flight while tile t is computed; one
+// barrier per tile. The loop is unrolled by two so that every LDS read names
+// a fixed buffer (the compiler then only waits for the copy at the barrier).
+// ---------------------------------------------------------------------------
+template <int D, typename OutT, bool PAGED>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
+  using M = Mfma32<bf16>;
+  constexpr int NS = D / 16;
+  constexpr int ND = D / 32;
+  using KT = PadTile<D, D / 8 + 1>;  // row reads
+  using VT = PadTile<D, D / 8 + 4>;  // transpose reads
+  static_assert(kFwdBN == 64, "tiles are 64 rows");
+  __shared__ __attribute__((aligned(1024))) bf16 sK0[KT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sV0[VT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sK1[KT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sV1[VT::ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 5, l32 = lane & 31, u = lane & 15, dh = (lane >> 4) & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rank = blockIdx.x / p.hq;
+  const int h = blockIdx.x - rank * p.hq;
+  if (rank >= *p.count) return;
+  const WorkItem it = p.items[p.order[rank]];
+  const int hk = h / p.group;
+  const MaskDev &m = p.m;
+
+  const int64_t r0 = it.q0 + 32 * w;
+  const int64_t row = r0 + l32;
+  const bool row_ok = row < it.q1;
+  const bool wave_on = r0 < it.q1;
+  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
+  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
+  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+
+  bf16x8 qf[NS];
+  {
+    const bf16 *qrow = (const bf16 *)p.q + row * p.q_st + h * p.q_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      i32x4 v = row_ok ? ld16(qrow + s * 16 + g * 8) : i32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x16 o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = f32x16{};
+  float mrow = neg_inf(), lsum = 0.f;
+
+  const bf16 *kb = (const bf16 *)p.k;
+  const bf16 *vb = (const bf16 *)p.v;
+  int koff[KT::NJ], voff[VT::NJ];
+  if constexpr (!PAGED) {
+    tile_voffsets<KT>(koff, p.k_st, w, lane);
+    tile_voffsets<VT>(voff, p.v_st, w, lane);
+  }
+  auto stage = [&](bf16 *sk, bf16 *sv, int64_t kt) {
+    if constexpr (!PAGED) {
+      const int nvalid = (int)(it.k1 - kt < kFwdBN ? it.k1 - kt : kFwdBN);
+      dma_tile_buf<KT>(sk, kb + kt * p.k_st + (int64_t)hk * p.k_sh, tile_bytes(p.k_st, nvalid, D), koff, w);
+      dma_tile_buf<VT>(sv, vb + kt * p.v_st + (int64_t)hk * p.v_sh, tile_bytes(p.v_st, nvalid, D), voff, w);
+    } else {
+      auto krow = [&](int r) -> const bf16 * {
+        int64_t j = kt + r;
+        j = j < it.k1 ? j : it.k1 - 1;  // rows past the end: a valid row, masked later
+        const bf16 *a = key_row<bf16>(p, kb, p.k_st, p.k_sh, j, hk);
+        return a ? a : kb;
+      };
+      auto vrow = [&](int r) -> const bf16 * {
+        int64_t j = kt + r;
+        j = j < it.k1 ? j : it.k1 - 1;
+        const bf16 *a = key_row<bf16>(p, vb, p.v_st, p.v_sh, j, hk);
+        return a ? a : vb;
+      };
+      dma_tile_rows<KT>(sk, krow, w, lane);
+      dma_tile_rows<VT>(sv, vrow, w, lane);
+    }
+  };
+
+  auto compute = [&](const bf16 *sk, const bf16 *sv, int64_t kt) {
+    if (!wave_on) return;
+    const int64_t klast = (kt + kFwdBN <= it.k1 ? kt + kFwdBN : it.k1) - 1;
+    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
+    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
+    if (m.causal && kp_lo > wq_hi) return;
+    if (m.window > 0 && kp_hi <= wq_lo - m.window) return;
+    const bool full = (kt + kFwdBN <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
+                      (m.window <= 0 || kp_lo > wq_hi - m.window);
+    f32x16 sc[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      // issue all of the sub-tile's K reads, then its MFMAs
+      bf16x8 kfr[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        kfr[s] = *reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + s * 16 + g * 8);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc = M::mma(kfr[s], qf[s], acc);
+      sc[sb] = acc;
+    }
+    if (!full) {
+      const int32_t t0 = (int32_t)(kt - it.kdoc0);
+      const int32_t nvalid = (int32_t)(it.k1 - kt);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t kk = sb * 32 + c_row(j, lane);
+          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
+          sc[sb][j] = vis ? sc[sb][j] : neg_inf();
+        }
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
+    mx = fmaxf(mx, xor32(mx));
+    const float mnew = fmaxf(mrow, mx * p.scale_log2);
+    const float muse = mnew == neg_inf() ? 0.f : mnew;
+    if (!__all(mnew == mrow)) {  // some row max moved: rescale
+      const float alpha = fast_exp2(mrow - muse);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) o[i] *= alpha;
+      mrow = mnew;
+    }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], p.scale_log2, -muse));
+        lsum += e;
+        pf[sb * 2 + (j >> 3)][j & 7] = (bf16)e;
+      }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      // issue the d-tile's 8 transpose reads, then its 4 MFMAs
+      bf16x8 va[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ra = t * 16 + 4 * g;
+        const int col = dt * 32 + dh * 16;
+        const bf16x4 lo = tile_tr4(sv, VT::PITCH, ra, col, u);
+        const bf16x4 hi = tile_tr4(sv, VT::PITCH, ra + 8, col, u);
+        va[t][0] = lo[0]; va[t][1] = lo[1]; va[t][2] = lo[2]; va[t][3] = lo[3];
+        va[t][4] = hi[0]; va[t][5] = hi[1]; va[t][6] = hi[2]; va[t][7] = hi[3];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[dt] = M::mma(va[t], pf[t], o[dt]);
+    }
+  };
+
+  if (it.k0 < it.k1) stage(sK0, sV0, it.k0);
+  __syncthreads();
+  for (int64_t kt = it.k0; kt < it.k1; kt += 2 * kFwdBN) {
+    if (kt + kFwdBN < it.k1) stage(sK1, sV1, kt + kFwdBN);
+    compute(sK0, sV0, kt);
+    __syncthreads();
+    if (kt + kFwdBN >= it.k1) break;
+    if (kt + 2 * kFwdBN < it.k1) stage(sK0, sV0, kt + 2 * kFwdBN);
+    compute(sK1, sV1, kt + kFwdBN);
+    __syncthreads();
+  }
+  if (!wave_on) return;
+
+  const float lt = lsum + xor32(lsum);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
+  if (!row_ok) return;
+  if (p.segmented) {
+    float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const int d0 = dt * 32 + 8 * j4 + 4 * g;
+        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
+        *reinterpret_cast<float4 *>(po + d0) = v4;
+      }
+    if (g == 0) p.part_lse[((int64_t)it.seg * p.hq + h) * p.n_q + row] = lse_v;
+    return;
+  }
+  OutT *orow = (OutT *)p.out + row * p.o_st + (int64_t)h * p.o_sh;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      if constexpr (sizeof(OutT) == 4) {
+        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
+        *reinterpret_cast<float4 *>(orow + d0) = v4;
+      } else {
+        bf16x4 v4;
+        v4[0] = (bf16)(o[dt][4 * j4] * inv); v4[1] = (bf16)(o[dt][4 * j4 + 1] * inv);
+        v4[2] = (bf16)(o[dt][4 * j4 + 2] * inv); v4[3] = (bf16)(o[dt][4 * j4 + 3] * inv);
+        *reinterpret_cast<bf16x4 *>(orow + d0) = v4;
+      }
+    }
+  if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
+}
+
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid, hipStream_t s) {
-  if (out_dtype == 0)
-    hipLaunchKernelGGL((fwd_kernel<T, D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-  else
-    hipLaunchKernelGGL((fwd_kernel<T, D, float>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+  if constexpr (sizeof(T) == 2) {
+    const bool paged = fp.block_table != nullptr;
+    if (out_dtype == 0) {
+      if (paged) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    } else {
+      if (paged) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    }
+  } else {
+    if (out_dtype == 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, float>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+  }
   return hipGetLastError();
 }
 

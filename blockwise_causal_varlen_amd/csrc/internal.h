@@ -129,6 +129,7 @@ struct BwdArgs {
   float scale;
   MaskDev mask;
   const float *lse, *delta;
+  const float *lse2;  // lse * log2(e), +inf for -inf (launch_lse2)
   int64_t n_q, n_k;
   float *dq; int64_t dq_st, dq_sh;
   float *dk; int64_t dk_st, dk_sh;
@@ -137,7 +138,8 @@ struct BwdArgs {
   SchedBufs ksched;   // tiles of key rows (dK/dV kernel)
   int64_t q_items, k_items;
 };
-hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s);  // 0: dK/dV, 1: dQ
+hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s);
+hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s);  // 0: dK/dV, 1: dQ
 
 hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int64_t n_src, void *dst,
                                int64_t d_st, int64_t d_sh, int64_t n_dst, int32_t elem_bytes,
