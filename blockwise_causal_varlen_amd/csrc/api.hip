@@ -3,6 +3,7 @@
 // drivers (zig-zag ring, contiguous ring, KV-parallel). No entry point reads
 // device memory on the host or synchronises, except attn_validate_inputs.
 #include <math.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -189,6 +190,16 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
   P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
+  // the kernels index rows and positions in 32 bits
+  const int64_t lim = (int64_t)1 << 30;
+  const int64_t R = (m && m->kv_interleave > 0) ? m->kv_interleave : 1;
+  if (P.n_q >= lim || P.n_k_logical >= lim || k->n_tok >= lim)
+    return fail(ATTN_ERR_UNSUPPORTED, "more than 2^30 rows");
+  if (m && (llabs(m->q_pos_offset) + P.n_q >= lim || llabs(m->k_pos_offset) + P.n_k_logical * R >= lim ||
+            m->window >= lim))
+    return fail(ATTN_ERR_UNSUPPORTED, "positions beyond 2^30");
+  if (k->stride_tok >= (1 << 22) || v->stride_tok >= (1 << 22))
+    return fail(ATTN_ERR_UNSUPPORTED, "key row stride of 2^22 elements or more");
   return ok();
 }
 

@@ -506,9 +506,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
+  constexpr int BN = kFwdBN;
   using KT = PadTile<D, D / 8 + 1>;  // row reads
   using VT = PadTile<D, D / 8 + 4>;  // transpose reads
-  static_assert(kFwdBN == 64, "tiles are 64 rows");
+  static_assert(BN == 64, "tiles are 64 rows");
+  // A row's reference max may trail its true max by up to this much (log2
+  // units) before the output is rescaled: probabilities stay <= 2^8, and the
+  // final lse = max + log2(sum) is exact for any reference.
+  constexpr float kRescaleSlack = 8.f;
   __shared__ __attribute__((aligned(1024))) bf16 sK0[KT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[VT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sK1[KT::ELEMS];
@@ -522,19 +527,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
   const int hk = h / p.group;
-  const MaskDev &m = p.m;
+  // every position and index fits in 32 bits (checked on the host)
+  const int32_t k1 = it.k1, kd0 = it.kdoc0, q1 = it.q1;
+  const int32_t causal = p.m.causal;
+  const int32_t W = (int32_t)p.m.window;
+  const int32_t qoff = (int32_t)p.m.q_pos_offset;
+  const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
+    if (RR == 0) return koff + t;
+    const int32_t b = t / BB;
+    return koff + (b * RR + rr) * BB + (t - b * BB);
+  };
 
-  const int64_t r0 = it.q0 + 32 * w;
-  const int64_t row = r0 + l32;
-  const bool row_ok = row < it.q1;
-  const bool wave_on = r0 < it.q1;
-  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
-  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
-  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+  const int32_t r0 = it.q0 + 32 * w;
+  const int32_t row = r0 + l32;
+  const bool row_ok = row < q1;
+  const bool wave_on = r0 < q1;
+  const int32_t qpos = qoff + (row - it.qdoc0);
+  const int32_t wq_lo = qoff + (r0 - it.qdoc0);
+  const int32_t wq_hi = qoff + ((r0 + 31 < q1 ? r0 + 31 : q1 - 1) - it.qdoc0);
 
   bf16x8 qf[NS];
   {
-    const bf16 *qrow = (const bf16 *)p.q + row * p.q_st + h * p.q_sh;
+    const bf16 *qrow = (const bf16 *)p.q + (int64_t)row * p.q_st + (int64_t)h * p.q_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       i32x4 v = row_ok ? ld16(qrow + s * 16 + g * 8) : i32x4{0, 0, 0, 0};
@@ -545,29 +561,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) o[i] = f32x16{};
   float mrow = neg_inf(), lsum = 0.f;
+  const float sl2 = p.scale_log2;
 
   const bf16 *kb = (const bf16 *)p.k;
   const bf16 *vb = (const bf16 *)p.v;
-  int koff[KT::NJ], voff[VT::NJ];
+  const int32_t kst = (int32_t)p.k_st, vst = (int32_t)p.v_st;
+  int koffs[KT::NJ], voffs[VT::NJ];
   if constexpr (!PAGED) {
-    tile_voffsets<KT>(koff, p.k_st, w, lane);
-    tile_voffsets<VT>(voff, p.v_st, w, lane);
+    tile_voffsets<KT>(koffs, kst, w, lane);
+    tile_voffsets<VT>(voffs, vst, w, lane);
   }
-  auto stage = [&](bf16 *sk, bf16 *sv, int64_t kt) {
+  // tile base pointers, advanced by one tile per stage
+  const bf16 *kp = kb + (int64_t)it.k0 * p.k_st + (int64_t)hk * p.k_sh;
+  const bf16 *vp = vb + (int64_t)it.k0 * p.v_st + (int64_t)hk * p.v_sh;
+  auto stage = [&](bf16 *sk, bf16 *sv, int32_t kt) {
     if constexpr (!PAGED) {
-      const int nvalid = (int)(it.k1 - kt < kFwdBN ? it.k1 - kt : kFwdBN);
-      dma_tile_buf<KT>(sk, kb + kt * p.k_st + (int64_t)hk * p.k_sh, tile_bytes(p.k_st, nvalid, D), koff, w);
-      dma_tile_buf<VT>(sv, vb + kt * p.v_st + (int64_t)hk * p.v_sh, tile_bytes(p.v_st, nvalid, D), voff, w);
+      const int32_t nvalid = k1 - kt < BN ? k1 - kt : BN;
+      dma_tile_buf<KT>(sk, kp, ((nvalid - 1) * kst + D) * 2, koffs, w);
+      dma_tile_buf<VT>(sv, vp, ((nvalid - 1) * vst + D) * 2, voffs, w);
+      kp += BN * (int64_t)kst;
+      vp += BN * (int64_t)vst;
     } else {
       auto krow = [&](int r) -> const bf16 * {
-        int64_t j = kt + r;
-        j = j < it.k1 ? j : it.k1 - 1;  // rows past the end: a valid row, masked later
+        int32_t j = kt + r;
+        j = j < k1 ? j : k1 - 1;  // rows past the end: a valid row, masked later
         const bf16 *a = key_row<bf16>(p, kb, p.k_st, p.k_sh, j, hk);
         return a ? a : kb;
       };
       auto vrow = [&](int r) -> const bf16 * {
-        int64_t j = kt + r;
-        j = j < it.k1 ? j : it.k1 - 1;
+        int32_t j = kt + r;
+        j = j < k1 ? j : k1 - 1;
         const bf16 *a = key_row<bf16>(p, vb, p.v_st, p.v_sh, j, hk);
         return a ? a : vb;
       };
@@ -576,15 +599,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  auto compute = [&](const bf16 *sk, const bf16 *sv, int64_t kt) {
+  auto compute = [&](const bf16 *sk, const bf16 *sv, int32_t kt) {
     if (!wave_on) return;
-    const int64_t klast = (kt + kFwdBN <= it.k1 ? kt + kFwdBN : it.k1) - 1;
-    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
-    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
-    if (m.causal && kp_lo > wq_hi) return;
-    if (m.window > 0 && kp_hi <= wq_lo - m.window) return;
-    const bool full = (kt + kFwdBN <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
-                      (m.window <= 0 || kp_lo > wq_hi - m.window);
+    const int32_t nvalid = k1 - kt;
+    const int32_t kp_lo = kpos(kt - kd0);
+    const int32_t kp_hi = kpos((nvalid < BN ? k1 : kt + BN) - 1 - kd0);
+    if (causal && kp_lo > wq_hi) return;
+    if (W > 0 && kp_hi <= wq_lo - W) return;
+    const bool full = (nvalid >= BN) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
     f32x16 sc[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -599,15 +621,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
       for (int s = 0; s < NS; ++s) acc = M::mma(kfr[s], qf[s], acc);
       sc[sb] = acc;
     }
-    if (!full) {
-      const int32_t t0 = (int32_t)(kt - it.kdoc0);
-      const int32_t nvalid = (int32_t)(it.k1 - kt);
+    if (!full) {  // wave-uniform
+      const int32_t t0 = kt - kd0;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int32_t kk = sb * 32 + c_row(j, lane);
-          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
+          const int32_t kpj = kpos(t0 + kk);
+          const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
           sc[sb][j] = vis ? sc[sb][j] : neg_inf();
         }
     }
@@ -617,21 +639,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
     mx = fmaxf(mx, xor32(mx));
-    const float mnew = fmaxf(mrow, mx * p.scale_log2);
-    const float muse = mnew == neg_inf() ? 0.f : mnew;
-    if (!__all(mnew == mrow)) {  // some row max moved: rescale
-      const float alpha = fast_exp2(mrow - muse);
+    const float mt = mx * sl2;
+    if (!__all(mt <= mrow + kRescaleSlack)) {  // some row outgrew its reference
+      const float mnew = fmaxf(mrow, mt);
+      const float alpha = fast_exp2(mrow - (mnew == neg_inf() ? 0.f : mnew));
       lsum *= alpha;
 #pragma unroll
       for (int i = 0; i < ND; ++i) o[i] *= alpha;
       mrow = mnew;
     }
+    const float muse = mrow == neg_inf() ? 0.f : mrow;
     bf16x8 pf[4];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], p.scale_log2, -muse));
+        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], sl2, -muse));
         lsum += e;
         pf[sb * 2 + (j >> 3)][j & 7] = (bf16)e;
       }
@@ -654,15 +677,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  if (it.k0 < it.k1) stage(sK0, sV0, it.k0);
+  if (it.k0 < k1) stage(sK0, sV0, it.k0);
   __syncthreads();
-  for (int64_t kt = it.k0; kt < it.k1; kt += 2 * kFwdBN) {
-    if (kt + kFwdBN < it.k1) stage(sK1, sV1, kt + kFwdBN);
+  for (int32_t kt = it.k0; kt < k1; kt += 2 * BN) {
+    if (kt + BN < k1) stage(sK1, sV1, kt + BN);
     compute(sK0, sV0, kt);
     __syncthreads();
-    if (kt + kFwdBN >= it.k1) break;
-    if (kt + 2 * kFwdBN < it.k1) stage(sK0, sV0, kt + 2 * kFwdBN);
-    compute(sK1, sV1, kt + kFwdBN);
+    if (kt + BN >= k1) break;
+    if (kt + 2 * BN < k1) stage(sK0, sV0, kt + 2 * BN);
+    compute(sK1, sV1, kt + BN);
     __syncthreads();
   }
   if (!wave_on) return;
@@ -684,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     if (g == 0) p.part_lse[((int64_t)it.seg * p.hq + h) * p.n_q + row] = lse_v;
     return;
   }
-  OutT *orow = (OutT *)p.out + row * p.o_st + (int64_t)h * p.o_sh;
+  OutT *orow = (OutT *)p.out + (int64_t)row * p.o_st + (int64_t)h * p.o_sh;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
