@@ -152,6 +152,21 @@ MaskDev mask_dev(const attn_mask *m) {
 
 TensorDev tdev(const attn_tensor *t) { return TensorDev{t->data, t->stride_tok, t->stride_head}; }
 
+// The kernels index rows, positions and in-tile offsets in 32 bits.
+static attn_status check_ranges(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                const attn_mask *m, int64_t n_k_logical) {
+  const int64_t lim = (int64_t)1 << 30;
+  const int64_t R = (m && m->kv_interleave > 0) ? m->kv_interleave : 1;
+  if (q->n_tok >= lim || n_k_logical >= lim || k->n_tok >= lim)
+    return fail(ATTN_ERR_UNSUPPORTED, "2^30 rows or more");
+  if (m && (llabs(m->q_pos_offset) + q->n_tok >= lim || llabs(m->k_pos_offset) + n_k_logical * R >= lim ||
+            m->window >= lim))
+    return fail(ATTN_ERR_UNSUPPORTED, "positions reach 2^30");
+  if (q->stride_tok >= (1 << 22) || k->stride_tok >= (1 << 22) || v->stride_tok >= (1 << 22))
+    return fail(ATTN_ERR_UNSUPPORTED, "a row stride of 2^22 elements or more");
+  return ok();
+}
+
 struct Problem {
   int64_t n_q, n_k_logical, hq, hkv, d;
   int64_t nseg;
@@ -190,17 +205,7 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
   P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
-  // the kernels index rows and positions in 32 bits
-  const int64_t lim = (int64_t)1 << 30;
-  const int64_t R = (m && m->kv_interleave > 0) ? m->kv_interleave : 1;
-  if (P.n_q >= lim || P.n_k_logical >= lim || k->n_tok >= lim)
-    return fail(ATTN_ERR_UNSUPPORTED, "more than 2^30 rows");
-  if (m && (llabs(m->q_pos_offset) + P.n_q >= lim || llabs(m->k_pos_offset) + P.n_k_logical * R >= lim ||
-            m->window >= lim))
-    return fail(ATTN_ERR_UNSUPPORTED, "positions beyond 2^30");
-  if (k->stride_tok >= (1 << 22) || v->stride_tok >= (1 << 22))
-    return fail(ATTN_ERR_UNSUPPORTED, "key row stride of 2^22 elements or more");
-  return ok();
+  return check_ranges(q, k, v, m, P.n_k_logical);
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -457,6 +462,8 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative sizes");
   if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
+  TRY(check_ranges(q, k, v, mask, k->n_tok));
+  if (dout->stride_tok >= (1 << 22)) return fail(ATTN_ERR_UNSUPPORTED, "a row stride of 2^22 elements or more");
   const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, delta == nullptr);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);

@@ -371,20 +371,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
   const int hk = blockIdx.x - rank * hkv_count;
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
-  const MaskDev &m = p.m;
+  // every position and index fits in 32 bits (checked on the host)
+  const int32_t q0 = it.q0, q1 = it.q1, qd0 = it.qdoc0, k1 = it.k1, kd0 = it.kdoc0;
+  const int32_t causal = p.m.causal;
+  const int32_t W = (int32_t)p.m.window;
+  const int32_t qoff = (int32_t)p.m.q_pos_offset;
+  const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
+    if (RR == 0) return koff + t;
+    const int32_t b = t / BB;
+    return koff + (b * RR + rr) * BB + (t - b * BB);
+  };
 
-  const int64_t kr0 = it.k0 + 32 * w;
-  const int64_t key = kr0 + l32;
-  const bool key_ok = key < it.k1;
-  const bool wave_on = kr0 < it.k1;
-  const int64_t kp_lane = m.pm.kpos(key - it.kdoc0);
-  const int64_t wk_lo = m.pm.kpos(kr0 - it.kdoc0);
-  const int64_t wk_hi = m.pm.kpos((kr0 + 31 < it.k1 ? kr0 + 31 : it.k1 - 1) - it.kdoc0);
+  const int32_t kr0 = it.k0 + 32 * w;
+  const int32_t key = kr0 + l32;
+  const bool key_ok = key < k1;
+  const bool wave_on = kr0 < k1;
+  const int32_t kp_lane = kpos(key - kd0);
+  const int32_t wk_lo = kpos(kr0 - kd0);
+  const int32_t wk_hi = kpos((kr0 + 31 < k1 ? kr0 + 31 : k1 - 1) - kd0);
 
   bf16x8 kf[NS], vf[NS];
   {
-    const bf16 *krow = (const bf16 *)p.k + key * p.k_st + (int64_t)hk * p.k_sh;
-    const bf16 *vrow = (const bf16 *)p.v + key * p.v_st + (int64_t)hk * p.v_sh;
+    const bf16 *krow = (const bf16 *)p.k + (int64_t)key * p.k_st + (int64_t)hk * p.k_sh;
+    const bf16 *vrow = (const bf16 *)p.v + (int64_t)key * p.v_st + (int64_t)hk * p.v_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       kf[s] = glob_row_frag<bf16>(krow, s, g, key_ok);
@@ -395,51 +406,61 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
-  int qoff[QT::NJ], ooff[QT::NJ];
-  tile_voffsets<QT>(qoff, p.q_st, w, lane);
-  tile_voffsets<QT>(ooff, p.do_st, w, lane);
-  const int nqt = (int)((it.q1 - it.q0 + QB - 1) / QB);
-  const int total = p.group * nqt;
+  int qoffs[QT::NJ], ooffs[QT::NJ];
+  tile_voffsets<QT>(qoffs, p.q_st, w, lane);
+  tile_voffsets<QT>(ooffs, p.do_st, w, lane);
+  const int32_t qst = (int32_t)p.q_st, ost = (int32_t)p.do_st;
+  const int32_t nqt = (q1 - q0 + QB - 1) / QB;
+  const int32_t total = p.group * nqt;
+  const int32_t h0 = hk * p.group;
   const bf16 *qb = (const bf16 *)p.q;
   const bf16 *ob = (const bf16 *)p.dout;
 
-  auto stage = [&](bf16 *sq, bf16 *so, float *sl, float *sd, int i) {
-    const int hh = i / nqt;
-    const int64_t qt = it.q0 + (int64_t)(i - hh * nqt) * QB;
-    const int h = hk * p.group + hh;
-    const int nvalid = (int)(it.q1 - qt < QB ? it.q1 - qt : QB);
-    dma_tile_buf<QT>(sq, qb + qt * p.q_st + (int64_t)h * p.q_sh, tile_bytes(p.q_st, nvalid, D), qoff, w);
-    dma_tile_buf<QT>(so, ob + qt * p.do_st + (int64_t)h * p.do_sh, tile_bytes(p.do_st, nvalid, D), ooff, w);
+  // (q head, tile start) of the next tile to stage and of the next to compute
+  int32_t sh = h0, sqt = q0, ch = h0, cqt = q0;
+  auto advance = [&](int32_t &h, int32_t &qt) {
+    qt += QB;
+    if (qt >= q1) { qt = q0; ++h; }
+  };
+
+  auto stage = [&](bf16 *sq, bf16 *so, float *sl, float *sd) {
+    const int32_t nvalid = q1 - sqt < QB ? q1 - sqt : QB;
+    dma_tile_buf<QT>(sq, qb + (int64_t)sqt * p.q_st + (int64_t)sh * p.q_sh, ((nvalid - 1) * qst + D) * 2, qoffs, w);
+    dma_tile_buf<QT>(so, ob + (int64_t)sqt * p.do_st + (int64_t)sh * p.do_sh, ((nvalid - 1) * ost + D) * 2, ooffs, w);
     if (w < 2) {
-      const float *src = (w == 0 ? p.lse2 : p.delta) + (int64_t)h * p.n_q + qt;
+      const float *src = (w == 0 ? p.lse2 : p.delta) + (int64_t)sh * p.n_q + sqt;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nvalid * 4, kBufFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(w == 0 ? sl : sd), 4, lane * 4, 0, 0, 0);
     }
+    advance(sh, sqt);
   };
 
-  auto compute = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd, int i) {
+  // One 64-row query tile against the wave's 32 keys. Rows past the end of the
+  // range hold zeros in Q and dO (and in lse2 / delta), so they add nothing.
+  auto compute = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd) {
+    const int32_t qt = cqt;
+    advance(ch, cqt);
     if (!wave_on) return;
-    const int hh = i / nqt;
-    const int64_t qt = it.q0 + (int64_t)(i - hh * nqt) * QB;
+    const int32_t qlast = (qt + QB <= q1 ? qt + QB : q1) - 1;
+    const int32_t qp_lo = qoff + (qt - qd0), qp_hi = qoff + (qlast - qd0);
+    if (causal && wk_lo > qp_hi) return;
+    if (W > 0 && wk_hi <= qp_lo - W) return;
+    const bool full = (!causal || wk_hi <= qp_lo) && (W <= 0 || wk_lo > qp_hi - W);
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int sub = 0; sub < QB / 32; ++sub) {
-      const int64_t qs0 = qt + sub * 32;
-      if (qs0 >= it.q1) break;
-      const int64_t qlast = (qs0 + 31 < it.q1 ? qs0 + 31 : it.q1 - 1);
-      const int64_t qp_lo = m.q_pos_offset + (qs0 - it.qdoc0);
-      const int64_t qp_hi = m.q_pos_offset + (qlast - it.qdoc0);
-      if (m.causal && wk_lo > qp_hi) continue;
-      if (m.window > 0 && wk_hi <= qp_lo - m.window) continue;
-      const bool full = (!m.causal || wk_hi <= qp_lo) && (m.window <= 0 || wk_lo > qp_hi - m.window);
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int sub = 0; sub < 2; ++sub) {
+      s[sub] = f32x16{};
+      dp[sub] = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         const int off = (sub * 32 + l32) * QT::PITCH + st * 16 + g * 8;
-        s = M::mma(*reinterpret_cast<const bf16x8 *>(sq + off), kf[st], s);
-        dp = M::mma(*reinterpret_cast<const bf16x8 *>(so + off), vf[st], dp);
+        s[sub] = M::mma(*reinterpret_cast<const bf16x8 *>(sq + off), kf[st], s[sub]);
+        dp[sub] = M::mma(*reinterpret_cast<const bf16x8 *>(so + off), vf[st], dp[sub]);
       }
-      float pv[16], ds[16];
-      const int64_t qp0 = m.q_pos_offset + (qt - it.qdoc0);
+    }
+    float pv[2][16], ds[2][16];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int q4 = sub * 32 + 8 * a + 4 * g;  // rows c_row(4a..4a+3)
@@ -448,34 +469,46 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * a + e;
-          const bool vis = full | visible(qp0 + q4 + e, kp_lane, m.causal, m.window);
-          const float ex = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -l4[e]));
-          pv[j] = vis ? ex : 0.f;
-          ds[j] = pv[j] * (dp[j] - d4[e]);
+          const float ex = fast_exp2(__builtin_fmaf(s[sub][j], p.scale_log2, -l4[e]));
+          pv[sub][j] = ex;
+          ds[sub][j] = ex * (dp[sub][j] - d4[e]);
         }
       }
+    if (!full) {  // wave-uniform
+      const int32_t qp_lane = qp_lo + 4 * g;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t qp = qp_lane + (sub * 32 + 8 * (j >> 2) + (j & 3));
+          const bool vis = ((causal == 0) | (kp_lane <= qp)) & ((W <= 0) | (kp_lane > qp - W));
+          pv[sub][j] = vis ? pv[sub][j] : 0.f;
+          ds[sub][j] = vis ? ds[sub][j] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        dv[dt] = acc_transposed<bf16>(dv[dt], so, QT::PITCH, sub * 32, dt, pv, lane);
-        dk[dt] = acc_transposed<bf16>(dk[dt], sq, QT::PITCH, sub * 32, dt, ds, lane);
+        dv[dt] = acc_transposed<bf16>(dv[dt], so, QT::PITCH, sub * 32, dt, pv[sub], lane);
+        dk[dt] = acc_transposed<bf16>(dk[dt], sq, QT::PITCH, sub * 32, dt, ds[sub], lane);
       }
-    }
   };
 
-  if (total > 0) stage(sQ0, sO0, sL0, sD0, 0);
+  if (total > 0) stage(sQ0, sO0, sL0, sD0);
   __syncthreads();
-  for (int i = 0; i < total; i += 2) {
-    if (i + 1 < total) stage(sQ1, sO1, sL1, sD1, i + 1);
-    compute(sQ0, sO0, sL0, sD0, i);
+  for (int32_t i = 0; i < total; i += 2) {
+    if (i + 1 < total) stage(sQ1, sO1, sL1, sD1);
+    compute(sQ0, sO0, sL0, sD0);
     __syncthreads();
     if (i + 1 >= total) break;
-    if (i + 2 < total) stage(sQ0, sO0, sL0, sD0, i + 2);
-    compute(sQ1, sO1, sL1, sD1, i + 1);
+    if (i + 2 < total) stage(sQ0, sO0, sL0, sD0);
+    compute(sQ1, sO1, sL1, sD1);
     __syncthreads();
   }
   if (!key_ok) return;
-  float *dkr = p.dk + key * p.dk_st + (int64_t)hk * p.dk_sh;
-  float *dvr = p.dv + key * p.dv_st + (int64_t)hk * p.dv_sh;
+  float *dkr = p.dk + (int64_t)key * p.dk_st + (int64_t)hk * p.dk_sh;
+  float *dvr = p.dv + (int64_t)key * p.dv_st + (int64_t)hk * p.dv_sh;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
