@@ -348,7 +348,7 @@ __global__ void lse2_kernel(const float *lse, float *lse2, int64_t n) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdParams p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -545,20 +545,31 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams p) {
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
   const int hk = h / p.group;
-  const MaskDev &m = p.m;
+  // every position and index fits in 32 bits (checked on the host)
+  const int32_t q1 = it.q1, k1 = it.k1, kd0 = it.kdoc0;
+  const int32_t causal = p.m.causal;
+  const int32_t W = (int32_t)p.m.window;
+  const int32_t qoff = (int32_t)p.m.q_pos_offset;
+  const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
+    if (RR == 0) return koff + t;
+    const int32_t b = t / BB;
+    return koff + (b * RR + rr) * BB + (t - b * BB);
+  };
 
-  const int64_t r0 = it.q0 + 32 * w;
-  const int64_t row = r0 + l32;
-  const bool row_ok = row < it.q1;
-  const bool wave_on = r0 < it.q1;
-  const int64_t qpos = m.q_pos_offset + (row - it.qdoc0);
-  const int64_t wq_lo = m.q_pos_offset + (r0 - it.qdoc0);
-  const int64_t wq_hi = m.q_pos_offset + ((r0 + 31 < it.q1 ? r0 + 31 : it.q1 - 1) - it.qdoc0);
+  const int32_t r0 = it.q0 + 32 * w;
+  const int32_t row = r0 + l32;
+  const bool row_ok = row < q1;
+  const bool wave_on = r0 < q1;
+  const int32_t qpos = qoff + (row - it.qdoc0);
+  const int32_t wq_lo = qoff + (r0 - it.qdoc0);
+  const int32_t wq_hi = qoff + ((r0 + 31 < q1 ? r0 + 31 : q1 - 1) - it.qdoc0);
 
   bf16x8 qf[NS], of[NS];
   {
-    const bf16 *qrow = (const bf16 *)p.q + row * p.q_st + (int64_t)h * p.q_sh;
-    const bf16 *orow = (const bf16 *)p.dout + row * p.do_st + (int64_t)h * p.do_sh;
+    const bf16 *qrow = (const bf16 *)p.q + (int64_t)row * p.q_st + (int64_t)h * p.q_sh;
+    const bf16 *orow = (const bf16 *)p.dout + (int64_t)row * p.do_st + (int64_t)h * p.do_sh;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       qf[s] = glob_row_frag<bf16>(qrow, s, g, row_ok);
@@ -567,68 +578,86 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(BwdParams p) {
   }
   const float lrow = row_ok ? p.lse2[(int64_t)h * p.n_q + row] : __builtin_inff();
   const float drow = row_ok ? p.delta[(int64_t)h * p.n_q + row] : 0.f;
+  const float sl2 = p.scale_log2;
   f32x16 dq[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) dq[i] = f32x16{};
 
-  int koff[KT::NJ], voff[VT::NJ];
-  tile_voffsets<KT>(koff, p.k_st, w, lane);
-  tile_voffsets<VT>(voff, p.v_st, w, lane);
-  const bf16 *kb = (const bf16 *)p.k;
-  const bf16 *vb = (const bf16 *)p.v;
-  auto stage = [&](bf16 *sk, bf16 *sv, int64_t kt) {
-    const int nvalid = (int)(it.k1 - kt < KB ? it.k1 - kt : KB);
-    dma_tile_buf<KT>(sk, kb + kt * p.k_st + (int64_t)hk * p.k_sh, tile_bytes(p.k_st, nvalid, D), koff, w);
-    dma_tile_buf<VT>(sv, vb + kt * p.v_st + (int64_t)hk * p.v_sh, tile_bytes(p.v_st, nvalid, D), voff, w);
+  const int32_t kst = (int32_t)p.k_st, vst = (int32_t)p.v_st;
+  int koffs[KT::NJ], voffs[VT::NJ];
+  tile_voffsets<KT>(koffs, kst, w, lane);
+  tile_voffsets<VT>(voffs, vst, w, lane);
+  // tile base pointers, advanced by one tile per stage
+  const bf16 *kp = (const bf16 *)p.k + (int64_t)it.k0 * p.k_st + (int64_t)hk * p.k_sh;
+  const bf16 *vp = (const bf16 *)p.v + (int64_t)it.k0 * p.v_st + (int64_t)hk * p.v_sh;
+  auto stage = [&](bf16 *sk, bf16 *sv, int32_t kt) {
+    const int32_t nvalid = k1 - kt < KB ? k1 - kt : KB;
+    dma_tile_buf<KT>(sk, kp, ((nvalid - 1) * kst + D) * 2, koffs, w);
+    dma_tile_buf<VT>(sv, vp, ((nvalid - 1) * vst + D) * 2, voffs, w);
+    kp += KB * (int64_t)kst;
+    vp += KB * (int64_t)vst;
   };
-  auto compute = [&](const bf16 *sk, const bf16 *sv, int64_t kt) {
+  // One 64-key tile against the wave's 32 query rows. Keys past the end of the
+  // range hold zeros in K and V; the unmasked path only runs on whole tiles.
+  auto compute = [&](const bf16 *sk, const bf16 *sv, int32_t kt) {
     if (!wave_on) return;
-    const int64_t klast = (kt + KB <= it.k1 ? kt + KB : it.k1) - 1;
-    const int64_t kp_lo = m.pm.kpos(kt - it.kdoc0);
-    const int64_t kp_hi = m.pm.kpos(klast - it.kdoc0);
-    if (m.causal && kp_lo > wq_hi) return;
-    if (m.window > 0 && kp_hi <= wq_lo - m.window) return;
-    const bool full = (kt + KB <= it.k1) && (!m.causal || kp_hi <= wq_lo) &&
-                      (m.window <= 0 || kp_lo > wq_hi - m.window);
-    const int32_t t0 = (int32_t)(kt - it.kdoc0);
-    const int32_t nvalid = (int32_t)(it.k1 - kt);
+    const int32_t nvalid = k1 - kt;
+    const int32_t kp_lo = kpos(kt - kd0);
+    const int32_t kp_hi = kpos((nvalid < KB ? k1 : kt + KB) - 1 - kd0);
+    if (causal && kp_lo > wq_hi) return;
+    if (W > 0 && kp_hi <= wq_lo - W) return;
+    const bool full = (nvalid >= KB) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int sb = 0; sb < KB / 32; ++sb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x16{};
+      dp[sb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s = M::mma(*reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8), qf[st], s);
-        dp = M::mma(*reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8), of[st], dp);
+        s[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8), qf[st], s[sb]);
+        dp[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8), of[st], dp[sb]);
       }
-      float ds[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ds[j] = fast_exp2(__builtin_fmaf(s[j], p.scale_log2, -lrow)) * (dp[j] - drow);
-      if (!full) {  // wave-uniform
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int32_t kk = sb * 32 + c_row(j, lane);
-          const bool vis = (kk < nvalid) & visible(qpos, m.pm.kpos32(t0 + kk), m.causal, m.window);
-          ds[j] = vis ? ds[j] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<bf16>(dq[dt], sk, KT::PITCH, sb * 32, dt, ds, lane);
     }
+    float ds[2][16];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ds[sb][j] = fast_exp2(__builtin_fmaf(s[sb][j], sl2, -lrow)) * (dp[sb][j] - drow);
+    if (!full) {  // wave-uniform
+      const int32_t t0 = kt - kd0;
+      auto mask = [&](auto kpos_of) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int32_t kk = sb * 32 + c_row(j, lane);
+            const int32_t kpj = kpos_of(t0 + kk);
+            const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            ds[sb][j] = vis ? ds[sb][j] : 0.f;
+          }
+      };
+      if (RR == 0) mask([&](int32_t t) { return koff + t; });
+      else mask(kpos);
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<bf16>(dq[dt], sk, KT::PITCH, sb * 32, dt, ds[sb], lane);
   };
 
-  if (it.k0 < it.k1) stage(sK0, sV0, it.k0);
+  if (it.k0 < k1) stage(sK0, sV0, it.k0);
   __syncthreads();
-  for (int64_t kt = it.k0; kt < it.k1; kt += 2 * KB) {
-    if (kt + KB < it.k1) stage(sK1, sV1, kt + KB);
+  for (int32_t kt = it.k0; kt < k1; kt += 2 * KB) {
+    if (kt + KB < k1) stage(sK1, sV1, kt + KB);
     compute(sK0, sV0, kt);
     __syncthreads();
-    if (kt + KB >= it.k1) break;
-    if (kt + 2 * KB < it.k1) stage(sK0, sV0, kt + 2 * KB);
+    if (kt + KB >= k1) break;
+    if (kt + 2 * KB < k1) stage(sK0, sV0, kt + 2 * KB);
     compute(sK1, sV1, kt + KB);
     __syncthreads();
   }
   if (!row_ok) return;
-  float *dqr = p.dq + row * p.dq_st + (int64_t)h * p.dq_sh;
+  float *dqr = p.dq + (int64_t)row * p.dq_st + (int64_t)h * p.dq_sh;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll

@@ -623,15 +623,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     }
     if (!full) {  // wave-uniform
       const int32_t t0 = kt - kd0;
+      auto mask = [&](auto kpos_of) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int32_t kk = sb * 32 + c_row(j, lane);
-          const int32_t kpj = kpos(t0 + kk);
-          const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
-          sc[sb][j] = vis ? sc[sb][j] : neg_inf();
-        }
+          for (int j = 0; j < 16; ++j) {
+            const int32_t kk = sb * 32 + c_row(j, lane);
+            const int32_t kpj = kpos_of(t0 + kk);
+            const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            sc[sb][j] = vis ? sc[sb][j] : neg_inf();
+          }
+      };
+      if (RR == 0) mask([&](int32_t t) { return koff + t; });
+      else mask(kpos);
     }
     float mx = neg_inf();
 #pragma unroll
