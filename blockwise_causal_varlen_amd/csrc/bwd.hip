@@ -367,8 +367,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hkv_count = p.hq / p.group;
-  const int rank = blockIdx.x / hkv_count;
-  const int hk = blockIdx.x - rank * hkv_count;
+  // logical index = (kv head, item): the items of one kv head are neighbours
+  const int lb = xcd_block();
+  const int cap = gridDim.x / hkv_count;
+  const int rank = lb % cap;
+  const int hk = lb / cap;
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
   // every position and index fits in 32 bits (checked on the host)
@@ -540,11 +543,15 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rank = blockIdx.x / p.hq;
-  const int h = blockIdx.x - rank * p.hq;
+  // logical index = (kv head, item, head in group), as in the forward
+  const int lb = xcd_block();
+  const int cap = gridDim.x / p.hq;
+  const int hg = lb % p.group, li = lb / p.group;
+  const int rank = li % cap;
+  const int hk = li / cap;
+  const int h = hk * p.group + hg;
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
-  const int hk = h / p.group;
   // every position and index fits in 32 bits (checked on the host)
   const int32_t q1 = it.q1, k1 = it.k1, kd0 = it.kdoc0;
   const int32_t causal = p.m.causal;

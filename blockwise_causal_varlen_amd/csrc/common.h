@@ -77,6 +77,15 @@ __device__ __forceinline__ void st16(void *p, i32x4 v) { *reinterpret_cast<i32x4
 // t is the index of the key inside its document's key buffer. The map is
 // strictly increasing in t, which the tile bounds rely on.
 // ---------------------------------------------------------------------------
+// Logical work-group index. Work-groups go to the chip's 8 XCDs round-robin;
+// this gives each XCD one contiguous range of logical indices, so work-groups
+// that read the same key/value rows run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_block() {
+  const int b = blockIdx.x, n = gridDim.x;
+  if (n % 8) return b;
+  return (b % 8) * (n / 8) + b / 8;
+}
+
 struct PosMap {
   int64_t k_pos_offset;
   int32_t interleave;  // R (0 = contiguous)

@@ -522,11 +522,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31, u = lane & 15, dh = (lane >> 4) & 1;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rank = blockIdx.x / p.hq;
-  const int h = blockIdx.x - rank * p.hq;
+  // logical index = (kv head, item, head in group): the heads that share a kv
+  // head, and the items of one kv head, are neighbours
+  const int lb = xcd_block();
+  const int cap = gridDim.x / p.hq;
+  const int hg = lb % p.group, li = lb / p.group;
+  const int rank = li % cap;
+  const int hk = li / cap;
+  const int h = hk * p.group + hg;
   if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
-  const int hk = h / p.group;
   // every position and index fits in 32 bits (checked on the host)
   const int32_t k1 = it.k1, kd0 = it.kdoc0, q1 = it.q1;
   const int32_t causal = p.m.causal;
