@@ -75,6 +75,65 @@ def load_traffic(kernel):
     return float(v) if v else None
 
 
+# rocprofv3 kernel names -> the library's timing names
+TRAFFIC_KERNELS = {"fwd_bf16_kernel": "attn_fwd", "dkdv_bf16_kernel": "attn_dkdv", "dq_bf16_kernel": "attn_dq",
+                   "merge_kernel": "attn_merge", "delta_kernel": "attn_delta", "decode_kernel": "attn_decode"}
+CALIB_BYTES = 1 << 30  # the plain device copy measured beside the kernels
+
+
+def calib_copy(torch):
+    """A plain device-to-device copy of CALIB_BYTES (3 times): what the HBM
+    counters read for it calibrates FETCH_SIZE / WRITE_SIZE."""
+    src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def traffic_summary(fetch_csv, write_csv, out_path, command):
+    """Per-launch HBM bytes of each kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each divided by what the
+    same counter reads for the plain copy of CALIB_BYTES."""
+    import csv
+    import statistics
+
+    def read(path, counter):
+        per = {}
+        calib = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, kib = r["Kernel_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name:
+                if kib * 1024 > CALIB_BYTES / 8:  # the big copy, not small runtime blits
+                    calib.append(kib * 1024 / CALIB_BYTES)
+                continue
+            for key, tname in TRAFFIC_KERNELS.items():
+                if key in name:
+                    per.setdefault(tname, []).append(kib * 1024)
+        if not calib:
+            raise SystemExit(f"{path}: no copy of {CALIB_BYTES} bytes found for the calibration")
+        return per, statistics.median(calib)
+
+    fetch, ff = read(fetch_csv, "FETCH_SIZE")
+    write, wf = read(write_csv, "WRITE_SIZE")
+    lines = ["# HBM traffic per launch from rocprofv3 counters (bytes); counter readings are",
+             "# divided by the reading for a plain device copy of %d bytes" % CALIB_BYTES,
+             "# commands:"] + ["#   " + c for c in command] + [
+             f"fetch_calibration = {ff:.4f}", f"write_calibration = {wf:.4f}", f"sources = {sources_digest()}"]
+    for tname in sorted(set(fetch) | set(write)):
+        fb = statistics.mean(fetch.get(tname, [0.0])) / ff
+        wb = statistics.mean(write.get(tname, [0.0])) / wf
+        lines += [f"{tname}.launches = {len(fetch.get(tname, []))}", f"{tname}.fetch_bytes_per_launch = {fb:.0f}",
+                  f"{tname}.write_bytes_per_launch = {wb:.0f}", f"{tname}.bytes_per_launch = {fb + wb:.0f}"]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def timed_steps(step, steps, warmup, torch, lib, timing=True):
     for _ in range(warmup):
         step()
@@ -242,9 +301,13 @@ def cpu_baseline(case, target_s, np):
                     pairs += len(sel) * (kb - ka)
         return dt, pairs
 
-    dt, _ = run(16)
-    n = int(min(2048, max(16, 16 * target_s / max(dt, 1e-3))))
+    # grow the sample until it takes about target_s (the cost per row is not
+    # linear at small samples: whole documents' keys are read per row chunk)
+    n = 16
     dt, pairs = run(n)
+    while dt < 0.6 * target_s and n < 8192:
+        n = min(8192, int(n * min(8.0, max(1.5, 0.9 * target_s / max(dt, 1e-3)))))
+        dt, pairs = run(n)
     hq, d = q.shape[1], q.shape[2]
     flops = pairs * (4 + 10) * d * hq
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -261,7 +324,17 @@ def main():
     ap.add_argument("--rows", choices=["all", "headline"], default="all")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for --traffic-summary)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn two rocprofv3 --pmc counter CSVs into profiles/traffic.txt")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="with --traffic-summary: a command line to record in the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
+                        os.path.join(ROOT, "profiles", "traffic.txt"), args.traffic_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the virtual-rank schedules run all ranks on a single device and "
@@ -284,6 +357,8 @@ def main():
     rows = other_rows(args, torch, lib, I, W) if args.rows == "all" else {}
     for k, v in rows.items():
         log(f"row {k}: {json.dumps({kk: vv for kk, vv in v.items() if kk != 'kernel_ms'})}")
+    if args.calib_copy:
+        calib_copy(torch)
     cpu = cpu_baseline(case, args.cpu_seconds, np) if args.cpu_baseline == "on" else None
     dom = h["kernels"][h["dominant"]]
     line = {

@@ -126,6 +126,8 @@ attn_status check_mask(const attn_mask *m) {
   if (m->kv_interleave < 0) return fail(ATTN_ERR_INVALID, "kv_interleave must be >= 0");
   if (m->kv_interleave > 0 && (m->block_size <= 0 || m->kv_rank < 0 || m->kv_rank >= m->kv_interleave))
     return fail(ATTN_ERR_INVALID, "round robin needs block_size > 0 and 0 <= kv_rank < kv_interleave");
+  if (m->kv_interleave > 0 && (m->block_size & (m->block_size - 1)))
+    return fail(ATTN_ERR_UNSUPPORTED, "round robin needs a power-of-two block_size");
   if (m->block_table && (m->block_size <= 0 || m->max_blocks <= 0 || m->page_stride <= 0))
     return fail(ATTN_ERR_INVALID, "paged keys need block_size, max_blocks and page_stride > 0");
   if (m->seg_size < 0) return fail(ATTN_ERR_INVALID, "seg_size must be >= 0");
@@ -147,6 +149,7 @@ MaskDev mask_dev(const attn_mask *m) {
   d.pm.interleave = m->kv_interleave;
   d.pm.rank = m->kv_rank;
   d.pm.block = m->block_size;
+  d.pm.shift = m->block_size > 0 ? __builtin_ctz((unsigned)m->block_size) : 0;
   return d;
 }
 

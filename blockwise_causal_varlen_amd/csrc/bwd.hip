@@ -380,11 +380,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   const int32_t W = (int32_t)p.m.window;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
-  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;
+  auto kpos_rr = [&](int32_t t) -> int32_t {  // round robin: block t >> SH sits at block R (t >> SH) + r
+    return koff + ((((t >> SH) * RR) + rr) << SH) + (t & ((1 << SH) - 1));
+  };
   auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
-    if (RR == 0) return koff + t;
-    const int32_t b = t / BB;
-    return koff + (b * RR + rr) * BB + (t - b * BB);
+    return RR == 0 ? koff + t : kpos_rr(t);
   };
 
   const int32_t kr0 = it.k0 + 32 * w;
@@ -558,11 +559,12 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   const int32_t W = (int32_t)p.m.window;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
-  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;
+  auto kpos_rr = [&](int32_t t) -> int32_t {  // round robin: block t >> SH sits at block R (t >> SH) + r
+    return koff + ((((t >> SH) * RR) + rr) << SH) + (t & ((1 << SH) - 1));
+  };
   auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
-    if (RR == 0) return koff + t;
-    const int32_t b = t / BB;
-    return koff + (b * RR + rr) * BB + (t - b * BB);
+    return RR == 0 ? koff + t : kpos_rr(t);
   };
 
   const int32_t r0 = it.q0 + 32 * w;
@@ -631,20 +633,30 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) ds[sb][j] = fast_exp2(__builtin_fmaf(s[sb][j], sl2, -lrow)) * (dp[sb][j] - drow);
     if (!full) {  // wave-uniform
-      const int32_t t0 = kt - kd0;
-      auto mask = [&](auto kpos_of) {
+      // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
+      const int32_t lim = nvalid - 4 * g;
+      const int32_t t0 = kt - kd0 + 4 * g;
+      if (RR == 0) {
+        const int32_t d = qpos - (koff + t0), dw = d - W;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int32_t kk = sb * 32 + c_row(j, lane);
-            const int32_t kpj = kpos_of(t0 + kk);
-            const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            const bool vis = (c < lim) & ((causal == 0) | (c <= d)) & ((W <= 0) | (c > dw));
             ds[sb][j] = vis ? ds[sb][j] : 0.f;
           }
-      };
-      if (RR == 0) mask([&](int32_t t) { return koff + t; });
-      else mask(kpos);
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            const int32_t kpj = kpos_rr(t0 + c);
+            const bool vis = (c < lim) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            ds[sb][j] = vis ? ds[sb][j] : 0.f;
+          }
+      }
     }
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)

@@ -61,9 +61,16 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Cross-lane exchange with lane l ^ 32 (the other half of a 32x32 tile column).
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// max / sum of a value and the one held by lane l ^ 32, in both lanes: one
+// v_permlane32_swap hands each half of the wave the other half's values (no
+// LDS round trip). Both lanes add in the same order, so they agree exactly.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 16-byte global load / store helpers.
@@ -91,6 +98,7 @@ struct PosMap {
   int32_t interleave;  // R (0 = contiguous)
   int32_t rank;
   int32_t block;       // B
+  int32_t shift;       // log2(B) (B is a power of two when R > 0)
   __device__ __forceinline__ int64_t kpos(int64_t t) const {
     if (interleave == 0) return k_pos_offset + t;
     int64_t b = t / block, o = t - b * block;

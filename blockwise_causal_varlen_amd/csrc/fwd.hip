@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair32_max(mx);
     const float mnew = fmaxf(mrow, mx * p.scale_log2);
     const float muse = mnew == neg_inf() ? 0.f : mnew;
     const float alpha = fast_exp2(mrow - muse);
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (!wave_on) return;
 
   // ---- epilogue: normalise, store out and lse
-  const float lt = lsum + xor32(lsum);
+  const float lt = pair32_sum(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
@@ -538,11 +538,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const int32_t W = (int32_t)p.m.window;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
-  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, BB = p.m.pm.block;
+  const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;
+  auto kpos_rr = [&](int32_t t) -> int32_t {  // round robin: block t >> SH sits at block R (t >> SH) + r
+    return koff + ((((t >> SH) * RR) + rr) << SH) + (t & ((1 << SH) - 1));
+  };
   auto kpos = [&](int32_t t) -> int32_t {  // key position of doc-local key t
-    if (RR == 0) return koff + t;
-    const int32_t b = t / BB;
-    return koff + (b * RR + rr) * BB + (t - b * BB);
+    return RR == 0 ? koff + t : kpos_rr(t);
   };
 
   const int32_t r0 = it.q0 + 32 * w;
@@ -627,27 +628,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
       sc[sb] = acc;
     }
     if (!full) {  // wave-uniform
-      const int32_t t0 = kt - kd0;
-      auto mask = [&](auto kpos_of) {
+      // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
+      // (a compile-time constant): compare c with per-lane bounds
+      const int32_t lim = nvalid - 4 * g;
+      const int32_t t0 = kt - kd0 + 4 * g;
+      if (RR == 0) {
+        const int32_t d = qpos - (koff + t0), dw = d - W;  // causal: c <= d; window: c > d - W
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int32_t kk = sb * 32 + c_row(j, lane);
-            const int32_t kpj = kpos_of(t0 + kk);
-            const bool vis = (kk < nvalid) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            const bool vis = (c < lim) & ((causal == 0) | (c <= d)) & ((W <= 0) | (c > dw));
             sc[sb][j] = vis ? sc[sb][j] : neg_inf();
           }
-      };
-      if (RR == 0) mask([&](int32_t t) { return koff + t; });
-      else mask(kpos);
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            const int32_t kpj = kpos_rr(t0 + c);
+            const bool vis = (c < lim) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
+            sc[sb][j] = vis ? sc[sb][j] : neg_inf();
+          }
+      }
     }
     float mx = neg_inf();
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair32_max(mx);
     const float mt = mx * sl2;
     if (!__all(mt <= mrow + kRescaleSlack)) {  // some row outgrew its reference
       const float mnew = fmaxf(mrow, mt);
@@ -699,7 +711,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   }
   if (!wave_on) return;
 
-  const float lt = lsum + xor32(lsum);
+  const float lt = pair32_sum(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;

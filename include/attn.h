@@ -133,7 +133,8 @@ typedef struct {
   int64_t k_pos_offset;
   int32_t kv_interleave;  /* R > 0: round-robin key positions; 0: contiguous */
   int32_t kv_rank;        /* r in [0, R) */
-  int32_t block_size;     /* page / round-robin block size in tokens */
+  int32_t block_size;     /* page / round-robin block size in tokens (a power of
+                             two when kv_interleave > 0) */
   int32_t max_blocks;     /* entries in block_table */
   const int32_t *block_table; /* device; NULL = not paged */
   int64_t page_stride;    /* elements between pages (paged only) */
