@@ -130,6 +130,8 @@ attn_status check_mask(const attn_mask *m) {
     return fail(ATTN_ERR_UNSUPPORTED, "round robin needs a power-of-two block_size");
   if (m->block_table && (m->block_size <= 0 || m->max_blocks <= 0 || m->page_stride <= 0))
     return fail(ATTN_ERR_INVALID, "paged keys need block_size, max_blocks and page_stride > 0");
+  if (m->block_table && (m->block_size & (m->block_size - 1)))
+    return fail(ATTN_ERR_UNSUPPORTED, "paged keys need a power-of-two block_size");
   if (m->seg_size < 0) return fail(ATTN_ERR_INVALID, "seg_size must be >= 0");
   if (m->seg_size > 0 && m->q_view != ATTN_VIEW_ALL)
     return fail(ATTN_ERR_UNSUPPORTED, "segments with a q view are not supported");

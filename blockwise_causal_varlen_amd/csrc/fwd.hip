@@ -495,6 +495,52 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
 }
 
+// Paged K/V tiles (block size 2^shift). Each lane's DMA block j of a tile
+// reads one row; paged_pages loads the physical page of that row for tile kt
+// (issued one tile ahead of the copy, so the table read is off the critical
+// path), dma_paged then copies the tile with those pages.
+template <typename TT>
+__device__ __forceinline__ int paged_row(int blk, int lane, int &col) {
+  const int s = blk * 64 + lane;
+  const int r = s / TT::NBLK, c = s - r * TT::NBLK;
+  col = c < TT::CPR ? c * 8 : 0;  // padding chunks re-read column 0 of their row
+  return c < TT::CPR ? r : 0;
+}
+template <typename TT>
+__device__ __forceinline__ void paged_pages(int (&pg)[TT::NJ], const int32_t *table, int32_t max_blocks, int shift,
+                                            int32_t kt, int32_t k1, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < TT::NJ; ++j) {
+    const int blk = wave + 4 * j;
+    if (blk < TT::NBLK) {
+      int col;
+      const int32_t r = paged_row<TT>(blk, lane, col);
+      const int32_t t = kt + r < k1 ? kt + r : k1 - 1;
+      const int32_t b = t >> shift;
+      pg[j] = table[b < max_blocks ? b : 0];
+    }
+  }
+}
+template <typename TT>
+__device__ __forceinline__ void dma_paged(bf16 *lds, const bf16 *base, int64_t page_stride, int64_t head_off,
+                                          int64_t st, const int (&pg)[TT::NJ], int32_t max_blocks, int64_t n_pages,
+                                          int shift, int32_t kt, int32_t k1, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < TT::NJ; ++j) {
+    const int blk = wave + 4 * j;
+    if (blk < TT::NBLK) {
+      int col;
+      const int32_t r = paged_row<TT>(blk, lane, col);
+      const int32_t t = kt + r < k1 ? kt + r : k1 - 1;  // rows past the end: a valid row, masked later
+      const int32_t b = t >> shift;
+      const int64_t page = pg[j];
+      const bool ok = b < max_blocks && page >= 0 && page < n_pages;
+      const bf16 *src = ok ? base + page * page_stride + head_off + (int64_t)(t & ((1 << shift) - 1)) * st + col : base;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16, 0, 0);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 forward: K/V tiles arrive by asynchronous global->LDS copies into two
 // swizzled buffers, so tile t+1 is in flight while tile t is computed; one
@@ -580,6 +626,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   // tile base pointers, advanced by one tile per stage
   const bf16 *kp = kb + (int64_t)it.k0 * p.k_st + (int64_t)hk * p.k_sh;
   const bf16 *vp = vb + (int64_t)it.k0 * p.v_st + (int64_t)hk * p.v_sh;
+  int kpg[KT::NJ], vpg[VT::NJ];  // paged keys: pages of the next tile to stage
+  if constexpr (PAGED) {
+    if (it.k0 < k1) {
+      paged_pages<KT>(kpg, p.block_table, p.max_blocks, SH, it.k0, k1, w, lane);
+      paged_pages<VT>(vpg, p.block_table, p.max_blocks, SH, it.k0, k1, w, lane);
+    }
+  }
   auto stage = [&](bf16 *sk, bf16 *sv, int32_t kt) {
     if constexpr (!PAGED) {
       const int32_t nvalid = k1 - kt < BN ? k1 - kt : BN;
@@ -588,20 +641,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
       kp += BN * (int64_t)kst;
       vp += BN * (int64_t)vst;
     } else {
-      auto krow = [&](int r) -> const bf16 * {
-        int32_t j = kt + r;
-        j = j < k1 ? j : k1 - 1;  // rows past the end: a valid row, masked later
-        const bf16 *a = key_row<bf16>(p, kb, p.k_st, p.k_sh, j, hk);
-        return a ? a : kb;
-      };
-      auto vrow = [&](int r) -> const bf16 * {
-        int32_t j = kt + r;
-        j = j < k1 ? j : k1 - 1;
-        const bf16 *a = key_row<bf16>(p, vb, p.v_st, p.v_sh, j, hk);
-        return a ? a : vb;
-      };
-      dma_tile_rows<KT>(sk, krow, w, lane);
-      dma_tile_rows<VT>(sv, vrow, w, lane);
+      dma_paged<KT>(sk, kb, p.page_stride, (int64_t)hk * p.k_sh, p.k_st, kpg, p.max_blocks, p.n_pages, SH, kt, k1, w,
+                    lane);
+      dma_paged<VT>(sv, vb, p.page_stride, (int64_t)hk * p.v_sh, p.v_st, vpg, p.max_blocks, p.n_pages, SH, kt, k1, w,
+                    lane);
+      if (kt + BN < k1) {  // the next tile's pages
+        paged_pages<KT>(kpg, p.block_table, p.max_blocks, SH, kt + BN, k1, w, lane);
+        paged_pages<VT>(vpg, p.block_table, p.max_blocks, SH, kt + BN, k1, w, lane);
+      }
     }
   };
 

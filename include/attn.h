@@ -134,7 +134,7 @@ typedef struct {
   int32_t kv_interleave;  /* R > 0: round-robin key positions; 0: contiguous */
   int32_t kv_rank;        /* r in [0, R) */
   int32_t block_size;     /* page / round-robin block size in tokens (a power of
-                             two when kv_interleave > 0) */
+                             two when kv_interleave > 0 or block_table is set) */
   int32_t max_blocks;     /* entries in block_table */
   const int32_t *block_table; /* device; NULL = not paged */
   int64_t page_stride;    /* elements between pages (paged only) */
