@@ -98,6 +98,34 @@ __device__ __forceinline__ f32x16 acc_transposed(f32x16 acc, const T *base, int 
   return acc;
 }
 
+// bf16 form over all ND d-tiles: acc[dt] += X^T(d rows dt*32.., k = 32 tile
+// rows from r0) * B, B in C layout in `pv`. Per 16-row half t the ND
+// MFMAs go back to back on independent accumulators.
+template <int ND>
+__device__ __forceinline__ void acc_transposed_all(f32x16 (&acc)[ND], const bf16 *base, int pitch, int r0,
+                                                   const float (&pv)[16], int lane) {
+  const int g = lane >> 5, u = lane & 15, dh = (lane >> 4) & 1;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)pv[t * 8 + e];
+    bf16x8 a[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const int ra = r0 + t * 16 + 4 * g + (u >> 2);
+      const int col = dt * 32 + dh * 16 + 4 * (u & 3);
+      i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + ra * pitch + col));
+      i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (ra + 8) * pitch + col));
+      bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+      a[dt][0] = l4[0]; a[dt][1] = l4[1]; a[dt][2] = l4[2]; a[dt][3] = l4[3];
+      a[dt][4] = h4[0]; a[dt][5] = h4[1]; a[dt][6] = h4[2]; a[dt][7] = h4[3];
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) acc[dt] = Mfma32<bf16>::mma(a[dt], b, acc[dt]);
+  }
+}
+
 // Stage rows [r0, r0 + nrows) (< lim valid) of a [tok, head, D] tensor into LDS.
 template <typename T, int D, int NROWS>
 __device__ __forceinline__ void stage_rows(T *dst, int pitch, const T *src, int64_t st, int64_t sh, int head,
@@ -491,12 +519,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
         }
     }
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        dv[dt] = acc_transposed<bf16>(dv[dt], so, QT::PITCH, sub * 32, dt, pv[sub], lane);
-        dk[dt] = acc_transposed<bf16>(dk[dt], sq, QT::PITCH, sub * 32, dt, ds[sub], lane);
-      }
+    for (int sub = 0; sub < 2; ++sub) {
+      acc_transposed_all<ND>(dv, so, QT::PITCH, sub * 32, pv[sub], lane);
+      acc_transposed_all<ND>(dk, sq, QT::PITCH, sub * 32, ds[sub], lane);
+    }
   };
 
   if (total > 0) stage(sQ0, sO0, sL0, sD0);
@@ -659,9 +685,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
       }
     }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) dq[dt] = acc_transposed<bf16>(dq[dt], sk, KT::PITCH, sb * 32, dt, ds[sb], lane);
+    for (int sb = 0; sb < 2; ++sb) acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds[sb], lane);
   };
 
   if (it.k0 < k1) stage(sK0, sV0, it.k0);

@@ -660,19 +660,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     if (causal && kp_lo > wq_hi) return;
     if (W > 0 && kp_hi <= wq_lo - W) return;
     const bool full = (nvalid >= BN) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
-    f32x16 sc[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      // issue all of the sub-tile's K reads, then its MFMAs
-      bf16x8 kfr[NS];
+    // the two 32-key sub-tiles' MFMAs alternate, so consecutive MFMAs never
+    // wait on each other's accumulator
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    {
+      bf16x8 kfr[2][NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        kfr[s] = *reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + s * 16 + g * 8);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 acc = f32x16{};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc = M::mma(kfr[s], qf[s], acc);
-      sc[sb] = acc;
+        for (int sb = 0; sb < 2; ++sb)
+          kfr[sb][s] = *reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + s * 16 + g * 8);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) sc[sb] = M::mma(kfr[sb][s], qf[s], sc[sb]);
     }
     if (!full) {  // wave-uniform
       // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
@@ -726,22 +727,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
         lsum += e;
         pf[sb * 2 + (j >> 3)][j & 7] = (bf16)e;
       }
+    // per 16-key chunk t: the ND d-tiles' transpose reads, then their MFMAs
+    // (independent accumulators back to back)
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      // issue the d-tile's 8 transpose reads, then its 4 MFMAs
-      bf16x8 va[4];
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 va[ND];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int dt = 0; dt < ND; ++dt) {
         const int ra = t * 16 + 4 * g;
         const int col = dt * 32 + dh * 16;
         const bf16x4 lo = tile_tr4(sv, VT::PITCH, ra, col, u);
         const bf16x4 hi = tile_tr4(sv, VT::PITCH, ra + 8, col, u);
-        va[t][0] = lo[0]; va[t][1] = lo[1]; va[t][2] = lo[2]; va[t][3] = lo[3];
-        va[t][4] = hi[0]; va[t][5] = hi[1]; va[t][6] = hi[2]; va[t][7] = hi[3];
+        va[dt][0] = lo[0]; va[dt][1] = lo[1]; va[dt][2] = lo[2]; va[dt][3] = lo[3];
+        va[dt][4] = hi[0]; va[dt][5] = hi[1]; va[dt][6] = hi[2]; va[dt][7] = hi[3];
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) o[dt] = M::mma(va[t], pf[t], o[dt]);
+      for (int dt = 0; dt < ND; ++dt) o[dt] = M::mma(va[dt], pf[t], o[dt]);
     }
   };
 
