@@ -45,7 +45,7 @@ NEG_INF = -np.inf
 __all__ = [
     "ALL", "FRONT", "BACK", "as_f64", "doc_bounds", "view_range",
     "key_position", "visibility", "block_forward", "block_backward",
-    "merge", "full_attention", "attention_grads",
+    "merge", "full_attention", "attention_grads", "eagle_forward", "eagle_grads",
     "zigzag_shard", "zigzag_unshard", "zigzag_global_positions",
     "zigzag_step", "zigzag_block_args", "zigzag_forward", "zigzag_backward",
     "ring_shard", "ring_forward", "ring_backward",
@@ -292,6 +292,99 @@ def attention_grads(dout, q, k, v, cu, scale):
     """Gradients of full causal per-document attention (block bwd over one block)."""
     out, lse = full_attention(q, k, v, cu, scale)
     return block_backward(dout, q, k, v, out, lse, cu, cu, scale, causal=True)
+
+
+# ----------------------------------------------------------------------------
+# EAGLE-3 mixed attention: block 0 causal over the sequence, TTT diagonals
+# ----------------------------------------------------------------------------
+def eagle_forward(q, ks, vs, cu, scale):
+    """Joint softmax of EAGLE-3 mixed attention -> (out, lse), by the definition.
+
+    [RING] `_CachedRingAttention` / [ZZ] `_CachedZigZagRingAttention`: cache
+    block 0 (ks[0], vs[0]) is the sequence, seen causally within each
+    document; every later block i >= 1 is a test-time-training step that gives
+    query t exactly one more key, ks[i][t], with value vs[i][t] (same
+    position). All keys enter one softmax:
+        s_tj   = scale <q_{t,h}, ks[0]_{j,g(h)}>      (causal keys j of t's doc)
+        d_it   = scale <q_{t,h}, ks[i]_{t,g(h)}>      (i = 1 .. n-1)
+        lse_t  = ln( sum_j e^{s_tj} + sum_i e^{d_it} )
+        out_t  = ( sum_j e^{s_tj} v0_j + sum_i e^{d_it} vi_t ) / e^{lse_t}
+    Global (unsharded) layout: q [n, HQ, D], ks/vs lists of [n, HKV, D].
+    """
+    q = as_f64(q)
+    ks = [as_f64(k) for k in ks]
+    vs = [as_f64(v) for v in vs]
+    n, hq, dim = q.shape
+    grp = hq // ks[0].shape[1]
+    out = np.zeros((n, hq, dim))
+    lse = np.full((hq, n), NEG_INF)
+    for qs, qe in doc_bounds(cu):
+        L = qe - qs
+        if L == 0:
+            continue
+        causal = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(hq):
+            g = h // grp
+            qd = q[qs:qe, h, :]
+            s = np.where(causal, scale * (qd @ ks[0][qs:qe, g, :].T), NEG_INF)
+            diag = [scale * np.sum(qd * k[qs:qe, g, :], axis=1) for k in ks[1:]]
+            allsc = np.concatenate([s] + [d_[:, None] for d_ in diag], axis=1)
+            mx = allsc.max(axis=1)
+            e = np.exp(allsc - mx[:, None])
+            tot = e.sum(axis=1)
+            lse[h, qs:qe] = mx + np.log(tot)
+            acc = e[:, :L] @ vs[0][qs:qe, g, :]
+            for i, v in enumerate(vs[1:]):
+                acc = acc + e[:, L + i][:, None] * v[qs:qe, g, :]
+            out[qs:qe, h, :] = acc / tot[:, None]
+    return out, lse
+
+
+def eagle_grads(dout, q, ks, vs, cu, scale):
+    """Gradients of the joint softmax of eagle_forward, by the definition.
+
+    The softmax over the augmented key set of each query (block-0 causal keys
+    plus one diagonal key per later block) has the usual gradient:
+        delta_t = <dout_t, out_t>,  P = e^{score - lse_t},  dP = <dout_t, value>,
+        dS = P (dP - delta_t);  dq_t += scale dS key;  dkey += scale dS q_t;
+        dvalue += P dout_t   (dk, dv summed over the q heads of a kv head)
+    For a diagonal key these sums have the single term of its own position,
+    the closed form [RING] `_CachedRingAttention` adds beside the block-0
+    backward. Returns (dq, dks list, dvs list).
+    """
+    q, dout = as_f64(q), as_f64(dout)
+    ks = [as_f64(k) for k in ks]
+    vs = [as_f64(v) for v in vs]
+    out, lse = eagle_forward(q, ks, vs, cu, scale)
+    n, hq, dim = q.shape
+    grp = hq // ks[0].shape[1]
+    dq = np.zeros_like(q)
+    dks = [np.zeros_like(k) for k in ks]
+    dvs = [np.zeros_like(v) for v in vs]
+    for qs, qe in doc_bounds(cu):
+        L = qe - qs
+        if L == 0:
+            continue
+        causal = np.tril(np.ones((L, L), dtype=bool))
+        for h in range(hq):
+            g = h // grp
+            qd, od, dd = q[qs:qe, h, :], out[qs:qe, h, :], dout[qs:qe, h, :]
+            l_t = lse[h, qs:qe]
+            delta = np.sum(dd * od, axis=1)
+            p = np.where(causal, np.exp(np.where(causal, scale * (qd @ ks[0][qs:qe, g, :].T), 0.0) - l_t[:, None]), 0.0)
+            dp = dd @ vs[0][qs:qe, g, :].T
+            ds = p * (dp - delta[:, None])
+            dq[qs:qe, h, :] += scale * (ds @ ks[0][qs:qe, g, :])
+            dks[0][qs:qe, g, :] += scale * (ds.T @ qd)
+            dvs[0][qs:qe, g, :] += p.T @ dd
+            for i in range(1, len(ks)):
+                kd, vd = ks[i][qs:qe, g, :], vs[i][qs:qe, g, :]
+                pi = np.exp(scale * np.sum(qd * kd, axis=1) - l_t)
+                dsi = pi * (np.sum(dd * vd, axis=1) - delta)
+                dq[qs:qe, h, :] += scale * dsi[:, None] * kd
+                dks[i][qs:qe, g, :] += scale * dsi[:, None] * qd
+                dvs[i][qs:qe, g, :] += pi[:, None] * dd
+    return dq, dks, dvs
 
 
 # ----------------------------------------------------------------------------

@@ -454,3 +454,97 @@ def test_decode_is_softmax_weighted_average():
             assert np.allclose(o[i, h], (w[:, None] * v[cu[i]:cu[i + 1], g]).sum(0), atol=1e-13)
     os_, ls_ = O.decode_forward(q, k, v, cu, 0.3, seqs=[2])
     assert np.allclose(os_[2], o[2]) and np.all(os_[0] == 0)
+
+
+# ----------------------------------------------------------------------------
+# EAGLE-3 mixed attention (block 0 causal + TTT diagonal blocks)
+# ----------------------------------------------------------------------------
+def _eagle_case(seed, lens, hq, hkv, d, nblk):
+    rng = np.random.default_rng(seed)
+    n = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = rng.standard_normal((n, hq, d))
+    ks = [rng.standard_normal((n, hkv, d)) for _ in range(nblk)]
+    vs = [rng.standard_normal((n, hkv, d)) for _ in range(nblk)]
+    return q, ks, vs, cu
+
+
+def _dense_masked_attention(q, keys, vals, mask, scale, grp):
+    """Brute force: one dense masked softmax per head over an explicit key list."""
+    n, hq, _ = q.shape
+    out = np.zeros_like(q)
+    lse = np.zeros((hq, n))
+    for h in range(hq):
+        g = h // grp
+        s = scale * q[:, h, :] @ keys[:, g, :].T
+        s = np.where(mask, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        w = np.exp(s - m)
+        lse[h] = (m[:, 0] + np.log(w.sum(axis=1)))
+        out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ vals[:, g, :]
+    return out, lse
+
+
+def test_eagle_equals_dense_augmented_keys():
+    # The joint softmax equals a dense masked softmax over the concatenated key
+    # list [block 0 rows | block 1 rows | ...] where query t sees the causal
+    # block-0 keys of its document and key t of every later block.
+    q, ks, vs, cu = _eagle_case(1, [5, 7, 4], 4, 2, 8, 4)
+    n = q.shape[0]
+    keys = np.concatenate(ks, axis=0)
+    vals = np.concatenate(vs, axis=0)
+    mask = np.zeros((n, n * len(ks)), dtype=bool)
+    for qs, qe in O.doc_bounds(cu):
+        for t in range(qs, qe):
+            mask[t, qs:t + 1] = True
+            for i in range(1, len(ks)):
+                mask[t, i * n + t] = True
+    scale = 0.3
+    ref_o, ref_l = _dense_masked_attention(q, keys, vals, mask, scale, 2)
+    out, lse = O.eagle_forward(q, ks, vs, cu, scale)
+    assert np.allclose(out, ref_o, atol=1e-12) and np.allclose(lse, ref_l, atol=1e-12)
+
+
+def test_eagle_without_diagonals_is_causal_attention():
+    q, ks, vs, cu = _eagle_case(2, [6, 3], 2, 1, 8, 1)
+    out, lse = O.eagle_forward(q, ks, vs, cu, 0.5)
+    ro, rl = O.full_attention(q, ks[0], vs[0], cu, 0.5)
+    assert np.allclose(out, ro, atol=1e-12) and np.allclose(lse, rl, atol=1e-12)
+
+
+def test_eagle_is_block0_merged_with_diagonal_partials():
+    # The pages' route: block 0's (out, lse) merged with each diagonal block's
+    # partial (block_out = v_i[t], block_lse = scale <q_t, k_i[t]>).
+    q, ks, vs, cu = _eagle_case(3, [4, 9], 4, 1, 8, 3)
+    scale = 0.25
+    out, lse = O.full_attention(q, ks[0], vs[0], cu, scale)
+    for k, v in zip(ks[1:], vs[1:]):
+        bl = scale * np.einsum("thd,thd->ht", q, np.repeat(k, 4, axis=1))
+        bo = np.repeat(v, 4, axis=1)
+        out, lse, _ = O.merge(out, lse, bo, bl)
+    eo, el = O.eagle_forward(q, ks, vs, cu, scale)
+    assert np.allclose(out, eo, atol=1e-12) and np.allclose(lse, el, atol=1e-12)
+
+
+def test_eagle_grads_match_finite_differences():
+    q, ks, vs, cu = _eagle_case(4, [3, 4], 2, 1, 4, 3)
+    rng = np.random.default_rng(5)
+    dout = rng.standard_normal(q.shape)
+    scale = 0.7
+    dq, dks, dvs = O.eagle_grads(dout, q, ks, vs, cu, scale)
+
+    def loss(q_, ks_, vs_):
+        return float(np.sum(dout * O.eagle_forward(q_, ks_, vs_, cu, scale)[0]))
+
+    eps = 1e-6
+    checks = [(q, dq, lambda x: (x, ks, vs))]
+    for i in range(len(ks)):
+        checks.append((ks[i], dks[i], lambda x, i=i: (q, ks[:i] + [x] + ks[i + 1:], vs)))
+        checks.append((vs[i], dvs[i], lambda x, i=i: (q, ks, vs[:i] + [x] + vs[i + 1:])))
+    for base, grad, build in checks:
+        for idx in [(0, 0, 0), (2, 1 if base.shape[1] > 1 else 0, 3), (6, 0, 1)]:
+            xp, xm = base.copy(), base.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            fd = (loss(*build(xp)) - loss(*build(xm))) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
