@@ -419,6 +419,75 @@ attn_status attn_merge_n(int32_t n_parts, const attn_tensor *parts_out, const fl
   return hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(a, s); }), "merge_n kernel");
 }
 
+static attn_status diag_common(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, DiagArgs &a) {
+  TRY(check_qkv(q, k, v));
+  if (k->n_tok != q->n_tok) return fail(ATTN_ERR_SHAPE, "a diagonal block needs k/v rows = q rows");
+  if (q->n_tok * q->n_head >= ((int64_t)1 << 31)) return fail(ATTN_ERR_UNSUPPORTED, "rows x heads reach 2^31");
+  a = DiagArgs{};
+  a.q = q->data; a.k = k->data; a.v = v->data; a.dtype = q->dtype;
+  a.q_st = q->stride_tok; a.q_sh = q->stride_head; a.k_st = k->stride_tok; a.k_sh = k->stride_head;
+  a.v_st = v->stride_tok; a.v_sh = v->stride_head;
+  a.n = (int32_t)q->n_tok; a.hq = (int32_t)q->n_head; a.group = (int32_t)(q->n_head / k->n_head);
+  a.d = (int32_t)q->head_dim;
+  return ok();
+}
+
+attn_status attn_merge_diag(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, float scale,
+                            const attn_tensor *out, float *lse, const attn_tensor *final_out, void *stream) {
+  DiagArgs a;
+  TRY(diag_common(q, k, v, a));
+  TRY(check_tensor(out, "out"));
+  if (out->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "running out must be f32");
+  if (out->n_tok != q->n_tok || out->n_head != q->n_head || out->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "out must be shaped like q");
+  if (final_out) {
+    TRY(check_tensor(final_out, "final_out"));
+    if (final_out->n_tok != q->n_tok || final_out->n_head != q->n_head || final_out->head_dim != q->head_dim)
+      return fail(ATTN_ERR_SHAPE, "final_out must be shaped like q");
+  }
+  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
+  a.out = (float *)out->data; a.o_st = out->stride_tok; a.o_sh = out->stride_head; a.lse = lse;
+  a.fout = final_out ? final_out->data : nullptr;
+  a.fout_dtype = final_out ? final_out->dtype : ATTN_F32;
+  a.f_st = final_out ? final_out->stride_tok : 0; a.f_sh = final_out ? final_out->stride_head : 0;
+  a.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_merge_diag", s, [&] { return launch_diag_merge(a, s); }), "diagonal merge kernel");
+}
+
+attn_status attn_diag_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                          const float *lse, const float *delta, float scale, const attn_tensor *dq,
+                          const attn_tensor *dk, const attn_tensor *dv, void *stream) {
+  DiagArgs a;
+  TRY(diag_common(q, k, v, a));
+  TRY(check_tensor(dout, "dout"));
+  if (dout->dtype != q->dtype) return fail(ATTN_ERR_DTYPE, "dout dtype differs from q");
+  if (dout->n_tok != q->n_tok || dout->n_head != q->n_head || dout->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "dout must be shaped like q");
+  if (!lse || !delta) return fail(ATTN_ERR_NULL, "lse / delta is NULL");
+  const attn_tensor *gr[3] = {dq, dk, dv};
+  const char *gn[3] = {"dq", "dk", "dv"};
+  for (int i = 0; i < 3; ++i) {
+    TRY(check_tensor(gr[i], gn[i]));
+    if (gr[i]->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "%s must be f32", gn[i]);
+  }
+  if (dq->n_tok != q->n_tok || dq->n_head != q->n_head || dq->head_dim != q->head_dim)
+    return fail(ATTN_ERR_SHAPE, "dq must be shaped like q");
+  for (int i = 1; i < 3; ++i)
+    if (gr[i]->n_tok != k->n_tok || gr[i]->n_head != k->n_head || gr[i]->head_dim != k->head_dim)
+      return fail(ATTN_ERR_SHAPE, "%s must be shaped like k", gn[i]);
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
+  a.dout = dout->data; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
+  a.lse = (float *)lse; a.delta = delta;
+  a.dq = (float *)dq->data; a.dq_st = dq->stride_tok; a.dq_sh = dq->stride_head;
+  a.dk = (float *)dk->data; a.dk_st = dk->stride_tok; a.dk_sh = dk->stride_head;
+  a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;
+  a.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_diag_bwd", s, [&] { return launch_diag_bwd(a, s); }), "diagonal backward kernel");
+}
+
 attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
   TRY(check_tensor(dout, "dout"));
   TRY(check_tensor(out, "out"));

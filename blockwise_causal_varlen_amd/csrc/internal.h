@@ -122,6 +122,26 @@ struct DeltaArgs {
 };
 hipError_t launch_delta(const DeltaArgs &a, hipStream_t s);
 
+// EAGLE-3 test-time-training diagonal blocks: row t of q head h sees the one
+// key k[t, h / group] of the block (forward merge and closed-form backward).
+struct DiagArgs {
+  const void *q, *k, *v;
+  int32_t dtype;  // of q, k, v (and dout)
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+  float *out; int64_t o_st, o_sh;  // f32 running output (forward)
+  float *lse;                      // [HQ, n]
+  void *fout; int32_t fout_dtype; int64_t f_st, f_sh;
+  const void *dout; int64_t do_st, do_sh;
+  const float *delta;
+  float *dq; int64_t dq_st, dq_sh;
+  float *dk; int64_t dk_st, dk_sh;
+  float *dv; int64_t dv_st, dv_sh;
+  int32_t n, hq, group, d;
+  float scale;
+};
+hipError_t launch_diag_merge(const DiagArgs &a, hipStream_t s);
+hipError_t launch_diag_bwd(const DiagArgs &a, hipStream_t s);
+
 struct BwdArgs {
   TensorDev q, k, v, dout;
   int32_t dtype;

@@ -122,6 +122,128 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// EAGLE-3 test-time-training diagonal blocks (NeMo AutoModel ring_attention,
+// `_CachedRingAttention`, `_merge_diag`): row t of q head h sees exactly one
+// key of such a block, k[t, g] (g = h / group), whose value is v[t, g]. The
+// block's partial is (block_out = v[t, g], block_lse = scale <q[t, h], k[t, g]>)
+// and merges into the running (out, lse) like any block. Its backward is the
+// one-key case of the joint-softmax gradient (given the merged lse, delta):
+//   p = exp(scale <q, k> - lse),  ds = p (<dout, v> - delta)
+//   dq[t, h] += scale ds k,  dk[t, g] += scale sum_h ds q,  dv[t, g] += sum_h p dout
+// A group of D/4 lanes owns one (row, head) (forward) or (row, kv head)
+// (backward, looping over the group's q heads: no atomics); each lane holds 4
+// elements and the dot products reduce across the group's lanes.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, G);
+  return x;
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+
+template <int D, typename T, typename FT>
+__global__ __launch_bounds__(256) void diag_merge_kernel(DiagArgs a) {
+  constexpr int G = D / 4;
+  const int32_t total = a.n * a.hq;
+  const int sub = threadIdx.x % G;
+  const int32_t per_blk = 256 / G;
+  for (int32_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += gridDim.x * per_blk) {
+    const int32_t row = pr / a.hq;
+    const int32_t h = pr - row * a.hq;
+    const int32_t g = h / a.group;
+    const f32x4 q4 = ld4<T>((const T *)a.q + row * a.q_st + h * a.q_sh + 4 * sub);
+    const f32x4 k4 = ld4<T>((const T *)a.k + row * a.k_st + g * a.k_sh + 4 * sub);
+    const f32x4 v4 = ld4<T>((const T *)a.v + row * a.v_st + g * a.v_sh + 4 * sub);
+    const float lb = a.scale * group_sum<G>(dot4(q4, k4));
+    const int64_t li = (int64_t)h * a.n + row;
+    const float la = a.lse[li];
+    float* orow = a.out + row * a.o_st + h * a.o_sh + 4 * sub;
+    f32x4 res;
+    float ln;
+    if (la == neg_inf()) {  // nothing merged yet for this row: the diagonal alone
+      res = v4;
+      ln = lb;
+    } else {
+      const f32x4 oa = ld4<float>(orow);
+      ln = fmaxf(la, lb) + log1pf(expf(-fabsf(la - lb)));
+      const float sig = expf(lb - ln);
+      res = oa - sig * (oa - v4);
+    }
+    st4<float>(orow, res);
+    if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub, res);
+    if (sub == 0) a.lse[li] = ln;
+  }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void diag_bwd_kernel(DiagArgs a) {
+  constexpr int G = D / 4;
+  const int32_t hkv = a.hq / a.group;
+  const int32_t total = a.n * hkv;
+  const int sub = threadIdx.x % G;
+  const int32_t per_blk = 256 / G;
+  for (int32_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += gridDim.x * per_blk) {
+    const int32_t row = pr / hkv;
+    const int32_t g = pr - row * hkv;
+    const f32x4 k4 = ld4<T>((const T *)a.k + row * a.k_st + g * a.k_sh + 4 * sub);
+    const f32x4 v4 = ld4<T>((const T *)a.v + row * a.v_st + g * a.v_sh + 4 * sub);
+    f32x4 dka = {0.f, 0.f, 0.f, 0.f}, dva = {0.f, 0.f, 0.f, 0.f};
+    for (int32_t hh = 0; hh < a.group; ++hh) {
+      const int32_t h = g * a.group + hh;
+      const f32x4 q4 = ld4<T>((const T *)a.q + row * a.q_st + h * a.q_sh + 4 * sub);
+      const f32x4 o4 = ld4<T>((const T *)a.dout + row * a.do_st + h * a.do_sh + 4 * sub);
+      const float s = a.scale * group_sum<G>(dot4(q4, k4));
+      const float dp = group_sum<G>(dot4(o4, v4));
+      const int64_t li = (int64_t)h * a.n + row;
+      const float l = a.lse[li];
+      const float pr_ = l == neg_inf() ? 0.f : expf(s - l);
+      const float ds = pr_ * (dp - a.delta[li]);
+      float *dqr = a.dq + row * a.dq_st + h * a.dq_sh + 4 * sub;
+      st4<float>(dqr, ld4<float>(dqr) + (a.scale * ds) * k4);
+      dka += ds * q4;
+      dva += pr_ * o4;
+    }
+    float *dkr = a.dk + row * a.dk_st + g * a.dk_sh + 4 * sub;
+    float *dvr = a.dv + row * a.dv_st + g * a.dv_sh + 4 * sub;
+    st4<float>(dkr, ld4<float>(dkr) + a.scale * dka);
+    st4<float>(dvr, ld4<float>(dvr) + dva);
+  }
+}
+
+template <int D>
+static hipError_t launch_diag_merge_d(const DiagArgs &a, hipStream_t s) {
+  const unsigned grid = stream_grid((int64_t)a.n * a.hq, 256 / (D / 4));
+  const bool fb = a.fout && a.fout_dtype == 0;
+  if (a.dtype == 0) {
+    if (fb) hipLaunchKernelGGL((diag_merge_kernel<D, bf16, bf16>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((diag_merge_kernel<D, bf16, float>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (fb) hipLaunchKernelGGL((diag_merge_kernel<D, float, bf16>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((diag_merge_kernel<D, float, float>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_merge(const DiagArgs &a, hipStream_t s) {
+  if ((int64_t)a.n * a.hq == 0) return hipSuccess;
+  return a.d == 128 ? launch_diag_merge_d<128>(a, s) : launch_diag_merge_d<64>(a, s);
+}
+
+template <int D>
+static hipError_t launch_diag_bwd_d(const DiagArgs &a, hipStream_t s) {
+  const unsigned grid = stream_grid((int64_t)a.n * (a.hq / a.group), 256 / (D / 4));
+  if (a.dtype == 0) hipLaunchKernelGGL((diag_bwd_kernel<D, bf16>), dim3(grid), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((diag_bwd_kernel<D, float>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_diag_bwd(const DiagArgs &a, hipStream_t s) {
+  if ((int64_t)a.n * a.hq == 0) return hipSuccess;
+  return a.d == 128 ? launch_diag_bwd_d<128>(a, s) : launch_diag_bwd_d<64>(a, s);
+}
+
+// ---------------------------------------------------------------------------
 // R-way merge (AWS NKI "Attention KV-Parallel Segmented CTE", Background:
 // the partials of the ranks are combined by online softmax):
 //   lse = m + log(sum_i exp(lse_i - m)),  out = sum_i exp(lse_i - lse) out_i

@@ -154,6 +154,26 @@ def small_zigzag(total, lo, hi, hq, hkv, d, dtype, cp, seed=0, loguniform=False)
 
 
 @dataclass
+class EagleCase:
+    """EAGLE-3 mixed attention: a zig-zag sequence problem (cache block 0) plus
+    n_ttt test-time-training blocks that hold one key/value per q row."""
+    base: ZigzagCase
+    ttt_k: list                 # n_ttt x [rows of q, HKV, D] (global rows, or q_rank's local rows)
+    ttt_v: list
+
+
+def eagle_case(base: ZigzagCase, n_ttt: int, seed=0):
+    """TTT blocks for `base`, drawn from their own seeded stream (k then v per block)."""
+    g = _gen(seed + 1000)
+    rows, hkv, d = base.q.shape[0], base.k.shape[1], base.k.shape[2]
+    ks, vs = [], []
+    for _ in range(n_ttt):
+        ks.append(normal((rows, hkv, d), base.k.dtype, g))
+        vs.append(normal((rows, hkv, d), base.k.dtype, g))
+    return EagleCase(base, ks, vs)
+
+
+@dataclass
 class KvpCase:
     """KV-parallel segmented prefill over R round-robin paged shards."""
     q: torch.Tensor              # [HQ, S, D] (NKI layout)

@@ -66,6 +66,8 @@ _SIGS = {
     "attn_merge_out_lse": (C.c_int, [T, P, T, P, P, I32, U32, P, T, I32, P]),
     "attn_merge_n": (C.c_int, [I32, T, C.POINTER(P), T, P, P]),
     "attn_bwd_delta": (C.c_int, [T, T, P, P]),
+    "attn_merge_diag": (C.c_int, [T, T, T, F, T, P, T, P]),
+    "attn_diag_bwd": (C.c_int, [T, T, T, T, P, P, F, T, T, T, P]),
     "attn_block_bwd": (C.c_int, [T, T, T, T, T, P, P, P, P, I32, I32, I32, M, F, T, T, T, P, SZ, P]),
     "attn_zigzag_shard": (C.c_int, [T, P, I32, I32, I32, I32, T, P]),
     "attn_zigzag_workspace_size": (C.c_int, [I32, T, T, I32, I32, C.POINTER(SZ)]),
@@ -267,6 +269,22 @@ def bwd_delta(dout, out, delta=None, stream=None):
     return delta
 
 
+def merge_diag(q, k, v, scale, out, lse, final_out=None, stream=None):
+    """attn_merge_diag: merge one per-position diagonal block (k, v rows = q rows)
+    into the f32 running `out` and `lse` (in place); optionally write `final_out`."""
+    _call("attn_merge_diag", C.byref(desc(q)), C.byref(desc(k)), C.byref(desc(v)), float(scale), C.byref(desc(out)),
+          lse.data_ptr(), C.byref(desc(final_out)) if final_out is not None else None, _stream(stream))
+    return out, lse
+
+
+def diag_bwd(dout, q, k, v, lse, delta, scale, dq, dk, dv, stream=None):
+    """attn_diag_bwd: ACCUMULATES the diagonal block's grads into dq, dk, dv (f32)."""
+    _call("attn_diag_bwd", C.byref(desc(dout)), C.byref(desc(q)), C.byref(desc(k)), C.byref(desc(v)),
+          lse.data_ptr(), delta.data_ptr(), float(scale), C.byref(desc(dq)), C.byref(desc(dk)), C.byref(desc(dv)),
+          _stream(stream))
+    return dq, dk, dv
+
+
 def block_bwd(dout, q, k, v, out, lse, cu_q, cu_k, max_q, max_k, scale, m: AttnMask | None = None, delta=None,
               dq=None, dk=None, dv=None, stream=None):
     """attn_block_bwd: ACCUMULATES into dq/dk/dv (f32; zero-initialised when not given)."""
@@ -311,6 +329,7 @@ class RingRunner:
         self.out = torch.empty(nq, hq, d, dtype=out_dtype or q.dtype, device=dev)
         self.lse = torch.empty(hq, nq, dtype=torch.float32, device=dev)
         self.qd, self.od, self.oad = desc(q), desc(self.out), desc(self.out_acc)
+        self.bwd_od = None  # the merged output the backward reads (default: self.out)
         self.kd = (AttnTensor * cp)(*[desc(t) for t in self.k_loc])
         self.vd = (AttnTensor * cp)(*[desc(t) for t in self.v_loc])
         n = SZ(0)
@@ -340,7 +359,8 @@ class RingRunner:
 
     def backward(self, stream=None):
         name = "attn_zigzag_bwd" if self.kind == "zigzag" else "attn_ring_bwd"
-        _call(name, self.cp, self.rank, C.byref(self.dod), C.byref(self.qd), self.kd, self.vd, C.byref(self.od),
+        _call(name, self.cp, self.rank, C.byref(self.dod), C.byref(self.qd), self.kd, self.vd,
+              C.byref(self.bwd_od if self.bwd_od is not None else self.od),
               self.lse.data_ptr(), self.cu.data_ptr(), self.ns, self.max_local, self.scale, C.byref(self.dqd),
               self.dkd, self.dvd, self.wp, self.wn, _stream(stream))
         return self.dq, self.dk, self.dv

@@ -72,7 +72,7 @@ def decode_bytes(k_lens, hq, hkv, d):
 class ZigzagWorkload:
     """cp virtual zig-zag ranks; `ranks` are the ones that run (all by default)."""
 
-    def __init__(self, case: I.ZigzagCase, ranks=None, device="cuda", with_bwd=False):
+    def __init__(self, case: I.ZigzagCase, ranks=None, device="cuda", with_bwd=False, out_dtype=None):
         self.case, self.cp = case, case.cp
         cp = case.cp
         self.ranks = list(range(cp)) if ranks is None else list(ranks)
@@ -100,7 +100,7 @@ class ZigzagWorkload:
                       if (with_bwd and case.dout is not None) else None)
             self.q_loc[r], self.dout_loc[r] = q, do
             self.runners[r] = L.RingRunner("zigzag", cp, r, q, self.k_loc, self.v_loc, self.cu_local,
-                                           self.max_local, case.scale, dout=do)
+                                           self.max_local, case.scale, dout=do, out_dtype=out_dtype)
 
     def forward(self):
         for r in self.ranks:
@@ -121,6 +121,78 @@ class ZigzagWorkload:
     def bwd_flops(self):
         hq, d = self.case.q.shape[1], self.case.q.shape[2]
         return 10 * d * hq * self.pairs_per_rank() * len(self.ranks)
+
+
+# ----------------------------------------------------------------------------
+# EAGLE-3 mixed attention (zig-zag block 0 + TTT diagonal blocks)
+# ----------------------------------------------------------------------------
+class EagleWorkload:
+    """Per virtual rank: cache block 0 runs the zig-zag ring (f32 merged state),
+    then each TTT block's per-position diagonal is merged (the last merge writes
+    the output in q's dtype). The backward feeds the final merged out and lse to
+    the block-0 ring backward and to each diagonal's closed-form backward."""
+
+    def __init__(self, case: I.EagleCase, ranks=None, device="cuda", with_bwd=False):
+        base = case.base
+        self.case, self.cp, self.n_ttt = case, base.cp, len(case.ttt_k)
+        if self.n_ttt < 1:
+            raise ValueError("at least one TTT block")
+        self.zz = ZigzagWorkload(base, ranks=ranks, device=device, with_bwd=with_bwd, out_dtype=torch.float32)
+        self.ranks = self.zz.ranks
+        self.tk, self.tv, self.final, self.dtk, self.dtv, self.delta = {}, {}, {}, {}, {}, {}
+        for r in self.ranks:
+            if base.q_rank is not None:
+                tk = [t.to(device) for t in case.ttt_k]
+                tv = [t.to(device) for t in case.ttt_v]
+            else:
+                tk = [L.zigzag_shard(t.to(device), self.zz.cu_global, self.cp, r, self.zz.max_len) for t in case.ttt_k]
+                tv = [L.zigzag_shard(t.to(device), self.zz.cu_global, self.cp, r, self.zz.max_len) for t in case.ttt_v]
+            self.tk[r], self.tv[r] = tk, tv
+            q = self.zz.q_loc[r]
+            self.final[r] = torch.empty(q.shape, dtype=q.dtype, device=device)
+            run = self.zz.runners[r]
+            run.bwd_od = L.desc(self.final[r])  # the backward reads the final merged output
+            if with_bwd:
+                self.dtk[r] = [torch.zeros(t.shape, dtype=torch.float32, device=device) for t in tk]
+                self.dtv[r] = [torch.zeros(t.shape, dtype=torch.float32, device=device) for t in tv]
+                self.delta[r] = torch.empty(q.shape[1], q.shape[0], dtype=torch.float32, device=device)
+
+    def forward(self):
+        sc = self.case.base.scale
+        for r in self.ranks:
+            run = self.zz.runners[r]
+            run.forward()  # block 0: run.out (f32) and run.lse hold the merged ring
+            for i in range(self.n_ttt):
+                L.merge_diag(self.zz.q_loc[r], self.tk[r][i], self.tv[r][i], sc, run.out, run.lse,
+                             final_out=self.final[r] if i == self.n_ttt - 1 else None)
+
+    def backward(self):
+        sc = self.case.base.scale
+        for r in self.ranks:
+            run = self.zz.runners[r]
+            run.zero_grads()
+            run.backward()  # block 0 with the final merged out and lse
+            L.bwd_delta(self.zz.dout_loc[r], self.final[r], delta=self.delta[r])
+            for i in range(self.n_ttt):
+                self.dtk[r][i].zero_()
+                self.dtv[r][i].zero_()
+                L.diag_bwd(self.zz.dout_loc[r], self.zz.q_loc[r], self.tk[r][i], self.tv[r][i], run.lse,
+                           self.delta[r], sc, run.dq, self.dtk[r][i], self.dtv[r][i])
+
+    def diag_bytes(self):
+        """HBM bytes of the diagonal kernels per rank (algorithmic): merge = q, k,
+        v reads + f32 out read/write + lse read/write per (row, head); the last
+        merge also writes the output in q's dtype. Backward = q, dout, k, v reads +
+        dq f32 read/write per (row, head) + dk, dv f32 read/write per (row, kv head)
+        + lse, delta reads."""
+        q = self.zz.q_loc[self.ranks[0]]
+        n, hq, d = q.shape
+        hkv = self.case.ttt_k[0].shape[1]
+        e = q.element_size()
+        merge = n * hq * (e * d + 8 * d + 8) + 2 * n * hkv * e * d
+        merge_last = merge + n * hq * e * d
+        bwd = n * hq * (2 * e * d + 8 * d + 8) + n * hkv * (2 * e * d + 16 * d)
+        return merge, merge_last, bwd
 
 
 # ----------------------------------------------------------------------------

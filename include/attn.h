@@ -218,6 +218,39 @@ attn_status attn_merge_n(int32_t n_parts, const attn_tensor *parts_out,
                          void *stream);
 
 /*
+ * attn_merge_diag -- merge one EAGLE-3 test-time-training diagonal block into
+ * the running (out, lse). [RING] `_CachedRingAttention` and `_merge_diag`
+ * (and [ZZ] `_CachedZigZagRingAttention`): cache block i >= 1 gives query row
+ * t exactly one key, k[t, g(h)], with value v[t, g(h)] (same position, any
+ * sharding), so its partial is
+ *     block_out[t, h] = v[t, g(h)],  block_lse[h, t] = scale <q[t,h], k[t,g(h)]>
+ * and it merges by the online-softmax identity (as attn_merge_out_lse).
+ *   q [n, HQ, D]; k, v [n, HKV, D]: all bf16 or all f32 (same rows as q)
+ *   out [n, HQ, D] f32 running output (read and written); lse [HQ, n] f32
+ *     (read and written; a row at -inf takes the diagonal alone)
+ *   final_out  NULL, or [n, HQ, D] bf16/f32 written with the merged output
+ *              (the cast of the last merge)
+ * Every row is merged. Errors: ATTN_ERR_SHAPE when k/v rows differ from q's.
+ */
+attn_status attn_merge_diag(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, float scale,
+                            const attn_tensor *out, float *lse, const attn_tensor *final_out, void *stream);
+
+/*
+ * attn_diag_bwd -- gradient of one diagonal block with the MERGED lse and
+ * delta ([RING] `_CachedRingAttention`: the diagonal grads are added in closed
+ * form beside the block-0 backward). Per row t and q head h, g = g(h):
+ *     p = exp(scale <q,k> - lse),  ds = p (<dout, v> - delta)
+ *     dq[t,h] += scale ds k[t,g];  dk[t,g] += scale sum_h ds q[t,h];
+ *     dv[t,g] += sum_h p dout[t,h]
+ *   dout, q [n, HQ, D]; k, v [n, HKV, D]: all bf16 or all f32
+ *   lse, delta [HQ, n] f32 (merged; delta from attn_bwd_delta on the merged out)
+ *   dq [n, HQ, D], dk, dv [n, HKV, D] f32, ACCUMULATED (+=); deterministic.
+ */
+attn_status attn_diag_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                          const float *lse, const float *delta, float scale, const attn_tensor *dq,
+                          const attn_tensor *dk, const attn_tensor *dv, void *stream);
+
+/*
  * attn_bwd_delta -- delta[h, i] = sum_d dout[i,h,d] * out[i,h,d] (f32), the
  * row term of the softmax backward, computed from the MERGED out; it is the
  * same for every block of a schedule, so a schedule computes it once.

@@ -340,7 +340,7 @@ def eagle_forward(q, ks, vs, cu, scale):
     return out, lse
 
 
-def eagle_grads(dout, q, ks, vs, cu, scale):
+def eagle_grads(dout, q, ks, vs, cu, scale, out=None, lse=None):
     """Gradients of the joint softmax of eagle_forward, by the definition.
 
     The softmax over the augmented key set of each query (block-0 causal keys
@@ -350,12 +350,16 @@ def eagle_grads(dout, q, ks, vs, cu, scale):
         dvalue += P dout_t   (dk, dv summed over the q heads of a kv head)
     For a diagonal key these sums have the single term of its own position,
     the closed form [RING] `_CachedRingAttention` adds beside the block-0
-    backward. Returns (dq, dks list, dvs list).
+    backward. ``out`` / ``lse`` (the merged state) default to eagle_forward's;
+    given, delta and P are taken from them, as a schedule's backward does.
+    Returns (dq, dks list, dvs list).
     """
     q, dout = as_f64(q), as_f64(dout)
     ks = [as_f64(k) for k in ks]
     vs = [as_f64(v) for v in vs]
-    out, lse = eagle_forward(q, ks, vs, cu, scale)
+    if out is None or lse is None:
+        out, lse = eagle_forward(q, ks, vs, cu, scale)
+    out, lse = as_f64(out), as_f64(lse)
     n, hq, dim = q.shape
     grp = hq // ks[0].shape[1]
     dq = np.zeros_like(q)
