@@ -21,6 +21,7 @@ The JSON line also carries
   * kernels: the same for every kernel of the step;
   * rows: the other workloads of the path measured the same way (packed
     varlen forward over 4 ranks, KV-parallel paged prefill for both windows,
+    EAGLE-3 mixed attention on the headline rank with 3 TTT diagonal blocks,
     one-query decode GB/s) -- skipped with --rows headline;
   * cpu_baseline: the fp64 oracle timed on the host on a bounded sample of
     the same workload (sampled query rows, forward and backward).
@@ -77,6 +78,7 @@ def load_traffic(kernel):
 
 # rocprofv3 kernel names -> the library's timing names
 TRAFFIC_KERNELS = {"fwd_bf16_kernel": "attn_fwd", "dkdv_bf16_kernel": "attn_dkdv", "dq_bf16_kernel": "attn_dq",
+                   "diag_merge_kernel": "attn_merge_diag", "diag_bwd_kernel": "attn_diag_bwd",
                    "merge_kernel": "attn_merge", "delta_kernel": "attn_delta", "decode_kernel": "attn_decode"}
 CALIB_BYTES = 1 << 30  # the plain device copy measured beside the kernels
 
@@ -111,9 +113,10 @@ def traffic_summary(fetch_csv, write_csv, out_path, command):
                 if kib * 1024 > CALIB_BYTES / 8:  # the big copy, not small runtime blits
                     calib.append(kib * 1024 / CALIB_BYTES)
                 continue
-            for key, tname in TRAFFIC_KERNELS.items():
+            for key, tname in TRAFFIC_KERNELS.items():  # first match (diag_merge before merge)
                 if key in name:
                     per.setdefault(tname, []).append(kib * 1024)
+                    break
         if not calib:
             raise SystemExit(f"{path}: no copy of {CALIB_BYTES} bytes found for the calibration")
         return per, statistics.median(calib)
@@ -244,6 +247,27 @@ def other_rows(args, torch, lib, I, W):
                                           "rank_merge": roofline("attn_merge_n", merge_bytes, kt, steps, "hbm"),
                                           "kernel_ms": kt}
         del w4, c4
+    # EAGLE-3 mixed attention on the headline rank: zig-zag block 0 + 3 TTT diagonals
+    n_ttt = 3
+    ce = I.eagle_case(I.cfg3(), n_ttt)
+    we = W.EagleWorkload(ce, ranks=[3], with_bwd=True)
+
+    def eagle_step():
+        we.forward()
+        we.backward()
+
+    sec, kt = timed_steps(eagle_step, steps, args.warmup, torch, lib)
+    nq, hq, d = we.zz.q_loc[3].shape
+    pairs = we.zz.pairs_per_rank() + nq * n_ttt
+    f = (4 + 10) * d * hq * pairs
+    mb, mbl, bb = we.diag_bytes()
+    rows[f"eagle_ttt{n_ttt}_fwd_bwd"] = {
+        "ms": sec * 1e3, "TFLOP/s": f / sec / 1e12, "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "merge_diag": roofline("attn_merge_diag", (n_ttt - 1) * mb + mbl, kt, steps, "hbm",
+                               load_traffic("attn_merge_diag")),
+        "diag_bwd": roofline("attn_diag_bwd", n_ttt * bb, kt, steps, "hbm", load_traffic("attn_diag_bwd")),
+        "kernel_ms": kt}
+    del we, ce
     torch.cuda.empty_cache()
     c5 = I.cfg5(device="cuda")
     w5 = W.DecodeWorkload(c5)
