@@ -46,6 +46,7 @@ __all__ = [
     "ALL", "FRONT", "BACK", "as_f64", "doc_bounds", "view_range",
     "key_position", "visibility", "block_forward", "block_backward",
     "merge", "full_attention", "attention_grads", "eagle_forward", "eagle_grads",
+    "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_lse_seq_to_head", "ulysses_lse_head_to_seq",
     "zigzag_shard", "zigzag_unshard", "zigzag_global_positions",
     "zigzag_step", "zigzag_block_args", "zigzag_forward", "zigzag_backward",
     "ring_shard", "ring_forward", "ring_backward",
@@ -389,6 +390,42 @@ def eagle_grads(dout, q, ks, vs, cu, scale, out=None, lse=None):
                 dks[i][qs:qe, g, :] += scale * dsi[:, None] * qd
                 dvs[i][qs:qe, g, :] += pi[:, None] * dd
     return dq, dks, dvs
+
+
+# ----------------------------------------------------------------------------
+# Ulysses all-to-all reshard (virtual ranks)
+# ----------------------------------------------------------------------------
+def ulysses_seq_to_head(locals_, uly):
+    """[ULY] `_gather_seq_scatter_heads`: uly sequence shards [S/uly, H, D]
+    (rank r holds rows r*S/uly ..) become uly head shards [S, H/uly, D] (rank r
+    holds heads r*H/uly ..): out[r][t, j] = locals_[t // (S/uly)][t % (S/uly), r*H/uly + j]."""
+    xs = [as_f64(x) for x in locals_]
+    full = np.concatenate(xs, axis=0)
+    hl = full.shape[1] // uly
+    return [full[:, r * hl:(r + 1) * hl] for r in range(uly)]
+
+
+def ulysses_head_to_seq(heads_, uly):
+    """[ULY] `_scatter_seq_gather_heads`, the inverse: uly head shards
+    [S, H/uly, D] become uly sequence shards [S/uly, H, D]."""
+    xs = [as_f64(x) for x in heads_]
+    full = np.concatenate(xs, axis=1)
+    sl = full.shape[0] // uly
+    return [full[r * sl:(r + 1) * sl] for r in range(uly)]
+
+
+def ulysses_lse_seq_to_head(lses, uly):
+    """[ULY] `_gather_lse`: [H, S/uly] per rank -> [H/uly, S] per rank (contiguous)."""
+    full = np.concatenate([as_f64(x) for x in lses], axis=1)
+    hl = full.shape[0] // uly
+    return [np.ascontiguousarray(full[r * hl:(r + 1) * hl]) for r in range(uly)]
+
+
+def ulysses_lse_head_to_seq(lses, uly):
+    """[ULY] `_scatter_lse`: [H/uly, S] per rank -> [H, S/uly] per rank."""
+    full = np.concatenate([as_f64(x) for x in lses], axis=0)
+    sl = full.shape[1] // uly
+    return [np.ascontiguousarray(full[:, r * sl:(r + 1) * sl]) for r in range(uly)]
 
 
 # ----------------------------------------------------------------------------

@@ -548,3 +548,32 @@ def test_eagle_grads_match_finite_differences():
             xm[idx] -= eps
             fd = (loss(*build(xp)) - loss(*build(xm))) / (2 * eps)
             assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (idx, fd, grad[idx])
+
+
+# ----------------------------------------------------------------------------
+# Ulysses all-to-all reshard
+# ----------------------------------------------------------------------------
+def test_ulysses_reshard_element_map_and_round_trip():
+    uly, S, H, D = 4, 12, 8, 3
+    # element value encodes (global row, head, d)
+    full = (np.arange(S)[:, None, None] * 1000 + np.arange(H)[None, :, None] * 10
+            + np.arange(D)[None, None, :]).astype(np.float64)
+    locals_ = [full[r * S // uly:(r + 1) * S // uly] for r in range(uly)]
+    heads = O.ulysses_seq_to_head(locals_, uly)
+    for r in range(uly):
+        assert heads[r].shape == (S, H // uly, D)
+        for t in range(S):
+            for j in range(H // uly):
+                assert heads[r][t, j, 0] == t * 1000 + (r * (H // uly) + j) * 10
+    back = O.ulysses_head_to_seq(heads, uly)
+    for r in range(uly):
+        assert np.array_equal(back[r], locals_[r])
+    lse = np.arange(H)[:, None] * 100.0 + np.arange(S)[None, :]
+    lloc = [lse[:, r * S // uly:(r + 1) * S // uly] for r in range(uly)]
+    lh = O.ulysses_lse_seq_to_head(lloc, uly)
+    for r in range(uly):
+        assert lh[r].flags["C_CONTIGUOUS"]
+        assert np.array_equal(lh[r], lse[r * (H // uly):(r + 1) * (H // uly)])
+    lb = O.ulysses_lse_head_to_seq(lh, uly)
+    for r in range(uly):
+        assert np.array_equal(lb[r], lloc[r])
