@@ -488,6 +488,58 @@ attn_status attn_diag_bwd(const attn_tensor *dout, const attn_tensor *q, const a
   return hip_check(timed("attn_diag_bwd", s, [&] { return launch_diag_bwd(a, s); }), "diagonal backward kernel");
 }
 
+attn_status attn_ulysses_reshard(int32_t uly, int32_t to_heads, const attn_tensor *src, const attn_tensor *dst,
+                                 void *stream) {
+  if (uly < 1 || uly > kMaxUly) return fail(ATTN_ERR_INVALID, "uly must be in [1, %d]", kMaxUly);
+  if (!src || !dst) return fail(ATTN_ERR_NULL, "NULL descriptor array");
+  for (int r = 0; r < uly; ++r) {
+    TRY(check_tensor(&src[r], "src"));
+    TRY(check_tensor(&dst[r], "dst"));
+    if (src[r].dtype != src[0].dtype || dst[r].dtype != src[0].dtype) return fail(ATTN_ERR_DTYPE, "dtypes differ");
+    if (src[r].n_tok != src[0].n_tok || src[r].n_head != src[0].n_head || src[r].head_dim != src[0].head_dim ||
+        dst[r].n_tok != dst[0].n_tok || dst[r].n_head != dst[0].n_head || dst[r].head_dim != src[0].head_dim)
+      return fail(ATTN_ERR_SHAPE, "every rank's shard must have the same shape");
+  }
+  const int64_t eb = src[0].dtype == ATTN_F32 ? 4 : 2;
+  ReshardArgs a{};
+  a.uly = uly; a.to_heads = to_heads ? 1 : 0;
+  a.row_bytes = (int32_t)(src[0].head_dim * eb);
+  if (to_heads) {  // src [S_l, H, D] -> dst [S, H / uly, D]
+    if (src[0].n_head % uly) return fail(ATTN_ERR_SHAPE, "heads must divide by uly");
+    if (dst[0].n_tok != src[0].n_tok * uly || dst[0].n_head != src[0].n_head / uly)
+      return fail(ATTN_ERR_SHAPE, "head shard must be [S_l * uly, H / uly, D]");
+    a.n_local = (int32_t)src[0].n_tok; a.h_local = (int32_t)dst[0].n_head;
+  } else {         // src [S, H_l, D] -> dst [S / uly, H_l * uly, D]
+    if (src[0].n_tok % uly) return fail(ATTN_ERR_SHAPE, "rows must divide by uly");
+    if (dst[0].n_tok * uly != src[0].n_tok || dst[0].n_head != src[0].n_head * uly)
+      return fail(ATTN_ERR_SHAPE, "sequence shard must be [S / uly, H_l * uly, D]");
+    a.n_local = (int32_t)dst[0].n_tok; a.h_local = (int32_t)src[0].n_head;
+  }
+  if ((int64_t)a.n_local * uly >= ((int64_t)1 << 31)) return fail(ATTN_ERR_UNSUPPORTED, "2^31 rows or more");
+  for (int r = 0; r < uly; ++r) {
+    a.src[r] = (const char *)src[r].data; a.s_st[r] = src[r].stride_tok * eb; a.s_sh[r] = src[r].stride_head * eb;
+    a.dst[r] = (char *)dst[r].data; a.d_st[r] = dst[r].stride_tok * eb; a.d_sh[r] = dst[r].stride_head * eb;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_reshard", s, [&] { return launch_reshard(a, s); }), "reshard kernel");
+}
+
+attn_status attn_ulysses_reshard_lse(int32_t uly, int32_t to_heads, const float *const *src, float *const *dst,
+                                     int64_t n_local, int64_t n_head, void *stream) {
+  if (uly < 1 || uly > kMaxUly) return fail(ATTN_ERR_INVALID, "uly must be in [1, %d]", kMaxUly);
+  if (!src || !dst) return fail(ATTN_ERR_NULL, "NULL pointer array");
+  if (n_local < 0 || n_head <= 0 || n_head % uly) return fail(ATTN_ERR_SHAPE, "heads must divide by uly");
+  if (n_local * uly >= ((int64_t)1 << 31)) return fail(ATTN_ERR_UNSUPPORTED, "2^31 rows or more");
+  LseReshardArgs a{};
+  a.uly = uly; a.to_heads = to_heads ? 1 : 0; a.n_local = (int32_t)n_local; a.h_local = (int32_t)(n_head / uly);
+  for (int r = 0; r < uly; ++r) {
+    if (!src[r] || !dst[r]) return fail(ATTN_ERR_NULL, "NULL lse pointer");
+    a.src[r] = src[r]; a.dst[r] = dst[r];
+  }
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_reshard", s, [&] { return launch_lse_reshard(a, s); }), "lse reshard kernel");
+}
+
 attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
   TRY(check_tensor(dout, "dout"));
   TRY(check_tensor(out, "out"));

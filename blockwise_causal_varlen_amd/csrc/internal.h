@@ -140,6 +140,21 @@ struct DiagArgs {
   float scale;
 };
 hipError_t launch_diag_merge(const DiagArgs &a, hipStream_t s);
+
+// Ulysses all-to-all between virtual ranks: sequence shards <-> head shards.
+constexpr int kMaxUly = 16;
+struct ReshardArgs {
+  const char *src[kMaxUly]; int64_t s_st[kMaxUly], s_sh[kMaxUly];  // strides in bytes
+  char *dst[kMaxUly]; int64_t d_st[kMaxUly], d_sh[kMaxUly];
+  int32_t uly, to_heads, row_bytes, n_local, h_local;
+};
+hipError_t launch_reshard(const ReshardArgs &a, hipStream_t s);
+struct LseReshardArgs {
+  const float *src[kMaxUly];
+  float *dst[kMaxUly];
+  int32_t uly, to_heads, n_local, h_local;
+};
+hipError_t launch_lse_reshard(const LseReshardArgs &a, hipStream_t s);
 hipError_t launch_diag_bwd(const DiagArgs &a, hipStream_t s);
 
 struct BwdArgs {

@@ -244,6 +244,75 @@ hipError_t launch_diag_bwd(const DiagArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Ulysses all-to-all between virtual ranks (NeMo AutoModel ulysses_attention,
+// `_gather_seq_scatter_heads` / `_scatter_seq_gather_heads`, `_gather_lse` /
+// `_scatter_lse`). With S_l = S / uly rows and H_l = H / uly heads per rank:
+//   to heads:  head shard r [S, H_l]:   row t, head j  <- sequence shard t / S_l,
+//              row t % S_l, head r H_l + j
+//   to rows:   the inverse.
+// Work-group (x, y = source rank, z = destination rank) copies the rows that go
+// from y to z, 16 bytes per lane; source and destination ranks are uniform, so
+// the per-rank pointers are read from the kernel arguments by scalar loads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void reshard_kernel(ReshardArgs a) {
+  const int sr = blockIdx.y, dr = blockIdx.z;
+  const int chunks = a.row_bytes / 16;
+  const int32_t per_row = a.h_local * chunks;
+  const int64_t total = (int64_t)a.n_local * per_row;
+  const char *src = a.src[sr];
+  char *dst = a.dst[dr];
+  const int64_t s_st = a.s_st[sr], s_sh = a.s_sh[sr], d_st = a.d_st[dr], d_sh = a.d_sh[dr];
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int32_t tl = (int32_t)(e / per_row);
+    const int32_t rem = (int32_t)(e - (int64_t)tl * per_row);
+    const int32_t j = rem / chunks, c = rem - j * chunks;
+    int64_t so, dof;
+    if (a.to_heads) {  // source: sequence shard sr; destination: head shard dr
+      so = tl * s_st + (int64_t)(dr * a.h_local + j) * s_sh;
+      dof = ((int64_t)sr * a.n_local + tl) * d_st + j * d_sh;
+    } else {           // source: head shard sr; destination: sequence shard dr
+      so = ((int64_t)dr * a.n_local + tl) * s_st + j * s_sh;
+      dof = tl * d_st + (int64_t)(sr * a.h_local + j) * d_sh;
+    }
+    st16(dst + dof + 16 * c, ld16(src + so + 16 * c));
+  }
+}
+
+__global__ __launch_bounds__(256) void lse_reshard_kernel(LseReshardArgs a) {
+  const int sr = blockIdx.y, dr = blockIdx.z;
+  const int64_t total = (int64_t)a.n_local * a.h_local;
+  const float *src = a.src[sr];
+  float *dst = a.dst[dr];
+  const int64_t n_full = (int64_t)a.n_local * a.uly;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int32_t j = (int32_t)(e / a.n_local);
+    const int32_t tl = (int32_t)(e - (int64_t)j * a.n_local);
+    if (a.to_heads)  // [H, S_l] of sequence shard sr -> [H_l, S] of head shard dr
+      dst[j * n_full + (int64_t)sr * a.n_local + tl] = src[(int64_t)(dr * a.h_local + j) * a.n_local + tl];
+    else             // [H_l, S] of head shard sr -> [H, S_l] of sequence shard dr
+      dst[(int64_t)(sr * a.h_local + j) * a.n_local + tl] = src[j * n_full + (int64_t)dr * a.n_local + tl];
+  }
+}
+
+hipError_t launch_reshard(const ReshardArgs &a, hipStream_t s) {
+  const int64_t per = (int64_t)a.n_local * a.h_local * (a.row_bytes / 16);
+  if (per == 0) return hipSuccess;
+  int64_t bx = (per + 255) / 256;
+  if (bx > 256) bx = 256;
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)bx, a.uly, a.uly), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_reshard(const LseReshardArgs &a, hipStream_t s) {
+  const int64_t per = (int64_t)a.n_local * a.h_local;
+  if (per == 0) return hipSuccess;
+  int64_t bx = (per + 255) / 256;
+  if (bx > 64) bx = 64;
+  hipLaunchKernelGGL(lse_reshard_kernel, dim3((unsigned)bx, a.uly, a.uly), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // R-way merge (AWS NKI "Attention KV-Parallel Segmented CTE", Background:
 // the partials of the ranks are combined by online softmax):
 //   lse = m + log(sum_i exp(lse_i - m)),  out = sum_i exp(lse_i - lse) out_i

@@ -67,6 +67,8 @@ _SIGS = {
     "attn_merge_n": (C.c_int, [I32, T, C.POINTER(P), T, P, P]),
     "attn_bwd_delta": (C.c_int, [T, T, P, P]),
     "attn_merge_diag": (C.c_int, [T, T, T, F, T, P, T, P]),
+    "attn_ulysses_reshard": (C.c_int, [I32, I32, T, T, P]),
+    "attn_ulysses_reshard_lse": (C.c_int, [I32, I32, P, P, I64, I64, P]),
     "attn_diag_bwd": (C.c_int, [T, T, T, T, P, P, F, T, T, T, P]),
     "attn_block_bwd": (C.c_int, [T, T, T, T, T, P, P, P, P, I32, I32, I32, M, F, T, T, T, P, SZ, P]),
     "attn_zigzag_shard": (C.c_int, [T, P, I32, I32, I32, I32, T, P]),
@@ -275,6 +277,24 @@ def merge_diag(q, k, v, scale, out, lse, final_out=None, stream=None):
     _call("attn_merge_diag", C.byref(desc(q)), C.byref(desc(k)), C.byref(desc(v)), float(scale), C.byref(desc(out)),
           lse.data_ptr(), C.byref(desc(final_out)) if final_out is not None else None, _stream(stream))
     return out, lse
+
+
+def ulysses_reshard(srcs, dsts, to_heads, stream=None):
+    """attn_ulysses_reshard over uly = len(srcs) virtual ranks (writes dsts)."""
+    uly = len(srcs)
+    sa = (AttnTensor * uly)(*[desc(t) for t in srcs])
+    da = (AttnTensor * uly)(*[desc(t) for t in dsts])
+    _call("attn_ulysses_reshard", uly, int(bool(to_heads)), sa, da, _stream(stream))
+    return dsts
+
+
+def ulysses_reshard_lse(srcs, dsts, to_heads, n_local, n_head, stream=None):
+    """attn_ulysses_reshard_lse: [H, S_l] per sequence shard <-> [H_l, S] per head shard."""
+    uly = len(srcs)
+    sp = (P * uly)(*[t.data_ptr() for t in srcs])
+    dp = (P * uly)(*[t.data_ptr() for t in dsts])
+    _call("attn_ulysses_reshard_lse", uly, int(bool(to_heads)), sp, dp, n_local, n_head, _stream(stream))
+    return dsts
 
 
 def diag_bwd(dout, q, k, v, lse, delta, scale, dq, dk, dv, stream=None):

@@ -196,6 +196,105 @@ class EagleWorkload:
 
 
 # ----------------------------------------------------------------------------
+# Ulysses (all-to-all) EAGLE-3 mixed attention
+# ----------------------------------------------------------------------------
+class UlyssesWorkload:
+    """uly virtual ranks, each holding a contiguous sequence shard (rows r S/uly ..)
+    of q, the block-0 K/V and the TTT blocks. Forward: the all-to-all reshard
+    gives each rank the FULL sequence for H/uly heads; block 0 is one varlen
+    causal block per rank over the full sequence with the GLOBAL cu_seqlens; the
+    inverse reshard brings (out, lse) back to the sequence shards, where the TTT
+    diagonals merge shard-locally. Backward: the merged output, dout and lse go
+    to head shards, block 0's backward runs on the merged state, its grads come
+    back by the inverse reshard, and the diagonals add their closed-form grads."""
+
+    def __init__(self, case: I.EagleCase, uly, device="cuda", with_bwd=False):
+        base = case.base
+        if base.q_rank is not None:
+            raise ValueError("Ulysses needs the whole sequence's q")
+        self.case, self.uly, self.n_ttt = case, uly, len(case.ttt_k)
+        S, hq, d = base.q.shape
+        hkv = base.k.shape[1]
+        if S % uly or hq % uly or hkv % uly:
+            raise ValueError("rows and heads must divide by uly")
+        self.S, self.sl, self.hq, self.hkv, self.d = S, S // uly, hq, hkv, d
+        dt = base.q.dtype
+        self.cu = base.cu.to(torch.int32).to(device)
+        self.max_len = int((base.cu[1:] - base.cu[:-1]).max())
+        sl = self.sl
+
+        def shards(x):
+            x = x.to(device)
+            return [x[r * sl:(r + 1) * sl] for r in range(uly)]
+
+        self.q_loc, self.k_loc, self.v_loc = shards(base.q), shards(base.k), shards(base.v)
+        self.tk = [shards(t) for t in case.ttt_k]   # [block][rank]
+        self.tv = [shards(t) for t in case.ttt_v]
+        emp = lambda *shape, dtype=dt: [torch.empty(*shape, dtype=dtype, device=device) for _ in range(uly)]
+        self.qh, self.kh, self.vh = emp(S, hq // uly, d), emp(S, hkv // uly, d), emp(S, hkv // uly, d)
+        self.oh = emp(S, hq // uly, d, dtype=torch.float32)
+        self.lh = emp(hq // uly, S, dtype=torch.float32)
+        self.out_loc = emp(sl, hq, d, dtype=torch.float32)
+        self.lse_loc = emp(hq, sl, dtype=torch.float32)
+        self.final = emp(sl, hq, d)
+        self.mask = L.mask(causal=True)
+        self.with_bwd = with_bwd
+        if with_bwd:
+            self.dout_loc = shards(base.dout)
+            self.dh, self.fh = emp(S, hq // uly, d), emp(S, hq // uly, d)
+            self.lse_h = emp(hq // uly, S, dtype=torch.float32)
+            self.dqh = emp(S, hq // uly, d, dtype=torch.float32)
+            self.dkh, self.dvh = emp(S, hkv // uly, d, dtype=torch.float32), emp(S, hkv // uly, d, dtype=torch.float32)
+            self.dq, self.dk, self.dv = (emp(sl, hq, d, dtype=torch.float32), emp(sl, hkv, d, dtype=torch.float32),
+                                         emp(sl, hkv, d, dtype=torch.float32))
+            self.delta = emp(hq, sl, dtype=torch.float32)
+            self.dtk = [emp(sl, hkv, d, dtype=torch.float32) for _ in range(self.n_ttt)]
+            self.dtv = [emp(sl, hkv, d, dtype=torch.float32) for _ in range(self.n_ttt)]
+
+    def forward(self):
+        sc, uly = self.case.base.scale, self.uly
+        L.ulysses_reshard(self.q_loc, self.qh, True)
+        L.ulysses_reshard(self.k_loc, self.kh, True)
+        L.ulysses_reshard(self.v_loc, self.vh, True)
+        for r in range(uly):
+            L.block_fwd(self.qh[r], self.kh[r], self.vh[r], self.cu, self.cu, self.max_len, self.max_len, sc,
+                        self.mask, out=self.oh[r], lse=self.lh[r])
+        L.ulysses_reshard(self.oh, self.out_loc, False)
+        L.ulysses_reshard_lse(self.lh, self.lse_loc, False, self.sl, self.hq)
+        for r in range(uly):
+            for i in range(self.n_ttt):
+                L.merge_diag(self.q_loc[r], self.tk[i][r], self.tv[i][r], sc, self.out_loc[r], self.lse_loc[r],
+                             final_out=self.final[r] if i == self.n_ttt - 1 else None)
+
+    def backward(self):
+        sc, uly = self.case.base.scale, self.uly
+        for r in range(uly):
+            L.bwd_delta(self.dout_loc[r], self.final[r], delta=self.delta[r])
+        L.ulysses_reshard(self.final, self.fh, True)
+        L.ulysses_reshard(self.dout_loc, self.dh, True)
+        L.ulysses_reshard_lse(self.lse_loc, self.lse_h, True, self.sl, self.hq)
+        for r in range(uly):
+            for t in (self.dqh[r], self.dkh[r], self.dvh[r]):
+                t.zero_()
+            L.block_bwd(self.dh[r], self.qh[r], self.kh[r], self.vh[r], self.fh[r], self.lse_h[r], self.cu, self.cu,
+                        self.max_len, self.max_len, sc, self.mask, dq=self.dqh[r], dk=self.dkh[r], dv=self.dvh[r])
+        L.ulysses_reshard(self.dqh, self.dq, False)
+        L.ulysses_reshard(self.dkh, self.dk, False)
+        L.ulysses_reshard(self.dvh, self.dv, False)
+        for r in range(uly):
+            for i in range(self.n_ttt):
+                self.dtk[i][r].zero_()
+                self.dtv[i][r].zero_()
+                L.diag_bwd(self.dout_loc[r], self.q_loc[r], self.tk[i][r], self.tv[i][r], self.lse_loc[r],
+                           self.delta[r], sc, self.dq[r], self.dtk[i][r], self.dtv[i][r])
+
+    def block0_pairs(self):
+        """Visible pairs per q head of block 0 (causal per document, all ranks)."""
+        lens = (self.case.base.cu[1:] - self.case.base.cu[:-1]).tolist()
+        return sum(L_ * (L_ + 1) // 2 for L_ in lens)
+
+
+# ----------------------------------------------------------------------------
 # KV-parallel
 # ----------------------------------------------------------------------------
 class KvpWorkload:

@@ -251,6 +251,29 @@ attn_status attn_diag_bwd(const attn_tensor *dout, const attn_tensor *q, const a
                           const attn_tensor *dk, const attn_tensor *dv, void *stream);
 
 /*
+ * attn_ulysses_reshard -- the Ulysses all-to-all between uly virtual ranks
+ * ([ULY] `_gather_seq_scatter_heads` / `_scatter_seq_gather_heads`). With
+ * S_l rows and H heads per sequence shard and H_l = H / uly:
+ *   to_heads != 0:  src[r] [S_l, H, D] (rank r's rows r S_l ..)  ->
+ *                   dst[r] [uly S_l, H_l, D] (all rows, heads r H_l ..)
+ *   to_heads == 0:  the inverse, src[r] [uly S_l, H_l, D] -> dst[r] [S_l, H, D]
+ *   src, dst  host arrays of uly descriptors (bf16 or f32, one shape each side)
+ * 1 <= uly <= 16. Errors: ATTN_ERR_SHAPE when heads / rows do not divide.
+ */
+attn_status attn_ulysses_reshard(int32_t uly, int32_t to_heads, const attn_tensor *src, const attn_tensor *dst,
+                                 void *stream);
+
+/*
+ * attn_ulysses_reshard_lse -- the same for the log-sum-exp ([ULY]
+ * `_gather_lse` / `_scatter_lse`): [H, S_l] per sequence shard <-> [H_l, uly S_l]
+ * per head shard, both contiguous f32 (the head-shard result is contiguous, as
+ * a backward that reads lse without strides needs).
+ *   src, dst  host arrays of uly device pointers; n_local = S_l; n_head = H
+ */
+attn_status attn_ulysses_reshard_lse(int32_t uly, int32_t to_heads, const float *const *src, float *const *dst,
+                                     int64_t n_local, int64_t n_head, void *stream);
+
+/*
  * attn_bwd_delta -- delta[h, i] = sum_d dout[i,h,d] * out[i,h,d] (f32), the
  * row term of the softmax backward, computed from the MERGED out; it is the
  * same for every block of a schedule, so a schedule computes it once.
