@@ -269,6 +269,30 @@ def other_rows(args, torch, lib, I, W):
         "kernel_ms": kt}
     del we, ce
     torch.cuda.empty_cache()
+    # Ulysses EAGLE-3 over the whole 131072-token sequence, uly = 8 virtual ranks
+    c3 = I.cfg3()
+    cu = c3.cu
+    full = I.zigzag_case("ulysses base", (cu[1:] - cu[:-1]).tolist(), c3.q.shape[1], c3.k.shape[1], c3.q.shape[2],
+                         c3.q.dtype, c3.cp)
+    del c3
+    cu_case = I.eagle_case(full, n_ttt)
+    wu = W.UlyssesWorkload(cu_case, 8, with_bwd=True)
+
+    def uly_step():
+        wu.forward()
+        wu.backward()
+
+    sec, kt = timed_steps(uly_step, max(2, steps // 2), 1, torch, lib)
+    nu = max(2, steps // 2)
+    f = (4 + 10) * wu.d * wu.hq * (wu.block0_pairs() + wu.S * n_ttt)
+    rows[f"ulysses_uly8_ttt{n_ttt}_fwd_bwd"] = {
+        "ms": sec * 1e3, "TFLOP/s": f / sec / 1e12, "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+        "workload": "131072 tokens (the headline documents), HQ=32, HKV=8, D=128, all 8 virtual ranks",
+        "reshard": roofline("attn_reshard", wu.reshard_bytes(), kt, nu, "hbm"),
+        "fwd_kernel": roofline("attn_fwd", 4 * wu.d * wu.hq * wu.block0_pairs(), kt, nu, "mfma"),
+        "kernel_ms": kt}
+    del wu, cu_case, full
+    torch.cuda.empty_cache()
     c5 = I.cfg5(device="cuda")
     w5 = W.DecodeWorkload(c5)
     sec, kt = timed_steps(w5.forward, steps, 1, torch, lib)

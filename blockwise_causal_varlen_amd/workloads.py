@@ -288,6 +288,16 @@ class UlyssesWorkload:
                 L.diag_bwd(self.dout_loc[r], self.q_loc[r], self.tk[i][r], self.tv[i][r], self.lse_loc[r],
                            self.delta[r], sc, self.dq[r], self.dtk[i][r], self.dtv[i][r])
 
+    def reshard_bytes(self):
+        """Bytes the reshards move per step (each element read once and written
+        once): forward q, k, v (q dtype), out (f32), lse; backward final out and
+        dout (q dtype), lse, dq, dk, dv (f32)."""
+        e = self.case.base.q.element_size()
+        S, hq, hkv, d = self.S, self.hq, self.hkv, self.d
+        fwd = S * d * (hq + 2 * hkv) * e + S * hq * d * 4 + S * hq * 4
+        bwd = 2 * S * hq * d * e + S * hq * 4 + S * d * (hq + 2 * hkv) * 4
+        return 2 * (fwd + (bwd if self.with_bwd else 0))
+
     def block0_pairs(self):
         """Visible pairs per q head of block 0 (causal per document, all ranks)."""
         lens = (self.case.base.cu[1:] - self.case.base.cu[:-1]).tolist()
