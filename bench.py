@@ -301,6 +301,15 @@ def other_rows(args, torch, lib, I, W):
                             "bytes": b, "decode_kernel": roofline("attn_decode", b, kt, steps, "hbm",
                                                                   load_traffic("attn_decode"))}
     del w5, c5
+    # split-KV (flash-decoding): 16 sequences x 65536 keys, HQ=32, HKV=4
+    c6 = I.long_decode([65536] * 16, device="cuda")
+    w6 = W.DecodeWorkload(c6)
+    sec, kt = timed_steps(w6.forward, steps, 1, torch, lib)
+    b = w6.bytes()
+    rows["decode_split_16x65536"] = {"ms": sec * 1e3, "GB/s": b / sec / 1e9, "frac": b / sec / 1e9 / PEAK_HBM_GBS,
+                                     "bytes": b, "decode_kernel": roofline("attn_decode", b, kt, steps, "hbm"),
+                                     "kernel_ms": kt}
+    del w6, c6
     torch.cuda.empty_cache()
     return rows
 

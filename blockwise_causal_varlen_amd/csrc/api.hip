@@ -177,6 +177,7 @@ struct Problem {
   int64_t nseg;
   bool decode;
   bool paged;
+  int32_t dsplit = 1, dsplit_len = 0;  // decode: split KV over dsplit waves per (sequence, kv head)
 };
 
 attn_status check_qkv(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v) {
@@ -210,13 +211,31 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
   P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
+  P.dsplit = 1; P.dsplit_len = 0;
+  if (P.decode) {
+    // flash-decoding split: when the (sequence, kv head) waves cannot fill the
+    // chip, each one's keys are split (>= 256 keys a split, at most 16 splits)
+    // and the partials merged, as segments are
+    const int64_t waves = (int64_t)num_seqs * P.hkv;
+    int64_t n = waves > 0 ? (2048 + waves - 1) / waves : 1;
+    if (n > 16) n = 16;
+    if (n > max_k / 256) n = max_k / 256;
+    if (n > 1) {
+      int64_t len = (max_k + n - 1) / n;
+      len = (len + 31) / 32 * 32;
+      P.dsplit = (int32_t)((max_k + len - 1) / len);
+      P.dsplit_len = (int32_t)len;
+    }
+  }
   return check_ranges(q, k, v, m, P.n_k_logical);
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs) {
-  if (P.decode) return 0;
+  if (P.decode)
+    return P.dsplit > 1 ? align256((size_t)P.dsplit * P.n_q * P.hq * P.d * 4) + align256((size_t)P.dsplit * P.hq * P.n_q * 4)
+                        : 0;
   const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
   size_t b = align256(sched_bytes(cap));
   if (P.nseg > 0) {
@@ -313,7 +332,15 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
     a.scale = scale; a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
     a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
     a.lse = lse; a.lse_n = P.n_q; a.n_k = k->n_tok;
-    return hip_check(timed("attn_decode", s, [&] { return launch_decode(a, s); }), "decode kernel");
+    if (P.dsplit <= 1)
+      return hip_check(timed("attn_decode", s, [&] { return launch_decode(a, s); }), "decode kernel");
+    char *w = (char *)workspace;
+    a.n_split = P.dsplit; a.split_len = P.dsplit_len;
+    a.part_out = (float *)w;
+    a.part_lse = (float *)(w + align256((size_t)P.dsplit * P.n_q * P.hq * P.d * 4));
+    TRY(hip_check(timed("attn_decode", s, [&] { return launch_decode(a, s); }), "decode kernel"));
+    return hip_check(timed("attn_decode_merge", s, [&] { return launch_decode_split_merge(a, s); }),
+                     "split-KV merge");
   }
 
   const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);

@@ -34,6 +34,10 @@ struct DecParams {
   void *out; int64_t o_st, o_sh;
   float *lse; int64_t lse_n;
   int64_t n_q, n_k;
+  // split KV: grid.z splits of split_len keys each; with n_split > 1 each
+  // wave writes a partial (out f32 [split][n_q][HQ][D], lse [split][HQ][n_q])
+  int32_t n_split, split_len;
+  float *part_out, *part_lse;
 };
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -60,7 +64,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
   int64_t k0 = p.cu_k[seq], k1 = p.cu_k[seq + 1];
   k0 = k0 < 0 ? 0 : (k0 > p.n_k ? p.n_k : k0);
   k1 = k1 < k0 ? k0 : (k1 > p.n_k ? p.n_k : k1);
-  const int64_t nk = k1 - k0;
+  // this wave's split of the sequence's keys
+  const int64_t ks = k0 + (int64_t)blockIdx.z * p.split_len;
+  const int64_t ke = k1 < ks + p.split_len ? k1 : ks + p.split_len;
+  const int64_t nk = ke > ks ? ke - ks : 0;
+  k0 = ks;
 
   // Q^T fragments: column u = q head hk*G + u (zero beyond the group).
   const bool col_ok = u < p.group;
@@ -183,6 +191,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
   lt += __shfl_xor(lt, 32, 64);
   if (!col_ok) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
+  if (p.n_split > 1) {  // partial of this split (an empty split: out 0, lse -inf)
+    float *po = p.part_out + ((int64_t)blockIdx.z * p.n_q + q0) * ((int64_t)p.hq * D) + (int64_t)hq_col * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d0 = dt * 16 + 4 * g;
+      float4 v4 = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+      *reinterpret_cast<float4 *>(po + d0) = v4;
+    }
+    if (g == 0) p.part_lse[((int64_t)blockIdx.z * p.hq + hq_col) * p.n_q + q0] = lse_v;
+    return;
+  }
   OutT *orow = (OutT *)p.out + q0 * p.o_st + (int64_t)hq_col * p.o_sh;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -197,8 +217,51 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
       *reinterpret_cast<bf16x4 *>(orow + d0) = v4;
     }
   }
-  if (g == 0)
-    p.lse[(int64_t)hq_col * p.lse_n + q0] = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
+  if (g == 0) p.lse[(int64_t)hq_col * p.lse_n + q0] = lse_v;
+}
+
+// Split-KV merge: per (sequence, q head) the n_split partials of its one row
+// combine by online softmax (lse = m + log sum exp(lse_i - m), out = sum
+// exp(lse_i - lse) out_i). Rows of no sequence stay untouched. D/4 lanes per
+// (sequence, head), 4 elements each.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void decode_split_merge_kernel(DecParams p) {
+  constexpr int G = D / 4;
+  const int sub = threadIdx.x % G;
+  const int64_t total = (int64_t)p.num_seqs * p.hq;
+  const int64_t per_blk = 256 / G;
+  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
+    const int32_t seq = (int32_t)(pr / p.hq);
+    const int32_t h = (int32_t)(pr - (int64_t)seq * p.hq);
+    const int64_t q0 = p.cu_q[seq], q1 = p.cu_q[seq + 1];
+    if (q1 <= q0 || q0 < 0 || q0 >= p.n_q) continue;
+    float m = neg_inf();
+    for (int z = 0; z < p.n_split; ++z) m = fmaxf(m, p.part_lse[((int64_t)z * p.hq + h) * p.n_q + q0]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    if (m != neg_inf()) {
+      for (int z = 0; z < p.n_split; ++z) {
+        const float lz = p.part_lse[((int64_t)z * p.hq + h) * p.n_q + q0];
+        const float wz = expf(lz - m);  // 0 for an empty split
+        if (wz > 0.f) {
+          const f32x4 oz = *reinterpret_cast<const f32x4 *>(
+              p.part_out + ((int64_t)z * p.n_q + q0) * ((int64_t)p.hq * D) + (int64_t)h * D + 4 * sub);
+          acc += wz * oz;
+          l += wz;
+        }
+      }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    OutT *orow = (OutT *)p.out + q0 * p.o_st + (int64_t)h * p.o_sh + 4 * sub;
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<f32x4 *>(orow) = acc * inv;
+    } else {
+      bf16x4 b;
+      b[0] = (bf16)(acc[0] * inv); b[1] = (bf16)(acc[1] * inv); b[2] = (bf16)(acc[2] * inv); b[3] = (bf16)(acc[3] * inv);
+      *reinterpret_cast<bf16x4 *>(orow) = b;
+    }
+    if (sub == 0) p.lse[(int64_t)h * p.lse_n + q0] = l > 0.f ? m + logf(l) : neg_inf();
+  }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
@@ -212,7 +275,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   p.lse = a.lse; p.lse_n = a.lse_n;
   p.n_q = a.lse_n;
   p.n_k = a.n_k;
-  dim3 grid((unsigned)a.num_seqs, (unsigned)((a.hkv + 3) / 4));
+  p.n_split = a.n_split > 1 ? a.n_split : 1;
+  p.split_len = a.n_split > 1 ? a.split_len : 0x7fffffff;
+  p.part_out = a.part_out; p.part_lse = a.part_lse;
+  dim3 grid((unsigned)a.num_seqs, (unsigned)((a.hkv + 3) / 4), (unsigned)p.n_split);
   if (a.num_seqs <= 0) return hipSuccess;
   if (a.head_dim == 128) {
     if (a.out_dtype == 0) hipLaunchKernelGGL((decode_kernel<128, bf16>), grid, dim3(256), 0, s, p);
@@ -220,6 +286,26 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   } else {
     if (a.out_dtype == 0) hipLaunchKernelGGL((decode_kernel<64, bf16>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((decode_kernel<64, float>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_split_merge(const DecodeArgs &a, hipStream_t s) {
+  DecParams p{};
+  p.cu_q = a.cu_q; p.hq = a.hq; p.num_seqs = a.num_seqs;
+  p.out = a.out; p.o_st = a.o_st; p.o_sh = a.o_sh;
+  p.lse = a.lse; p.lse_n = a.lse_n; p.n_q = a.lse_n;
+  p.n_split = a.n_split; p.part_out = a.part_out; p.part_lse = a.part_lse;
+  if (a.num_seqs <= 0) return hipSuccess;
+  const int G = a.head_dim / 4;
+  int64_t blocks = ((int64_t)a.num_seqs * a.hq + 256 / G - 1) / (256 / G);
+  if (blocks > 8192) blocks = 8192;
+  if (a.head_dim == 128) {
+    if (a.out_dtype == 0) hipLaunchKernelGGL((decode_split_merge_kernel<128, bf16>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_split_merge_kernel<128, float>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  } else {
+    if (a.out_dtype == 0) hipLaunchKernelGGL((decode_split_merge_kernel<64, bf16>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_split_merge_kernel<64, float>), dim3((unsigned)blocks), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -86,8 +86,11 @@ struct DecodeArgs {
   void *out; int32_t out_dtype; int64_t o_st, o_sh;
   float *lse; int64_t lse_n;
   int64_t n_k;
+  int32_t n_split = 1, split_len = 0;      // split KV (flash-decoding) when n_split > 1
+  float *part_out = nullptr, *part_lse = nullptr;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_split_merge(const DecodeArgs &a, hipStream_t s);
 
 struct MergeArgs {
   float *out; int64_t o_st, o_sh;          // running f32 state

@@ -236,3 +236,25 @@ def cfg5(device="cpu", nseq=65536, max_len=2048, hq=32, hkv=4, d=128, seed=0):
         v = normal((total, hkv, d), torch.bfloat16, g)
     scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     return DecodeCase(q.to(device), k, v, cu.to(torch.int32), lens, scale)
+
+
+def long_decode(lens, hq=32, hkv=4, d=128, seed=0, device="cpu"):
+    """One-query decode with given (long) key lengths: the split-KV regime where
+    the (sequence, kv head) pairs alone cannot fill the chip."""
+    g = _gen(seed)
+    lens = torch.tensor(lens, dtype=torch.int64)
+    nseq = lens.numel()
+    cu = torch.zeros(nseq + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(lens, 0)
+    q = normal((nseq, hq, d), torch.bfloat16, g)
+    total = int(cu[-1])
+    if str(device).startswith("cuda"):
+        gd = torch.Generator(device=device)
+        gd.manual_seed(seed)
+        k = normal_chunked((total, hkv, d), gd, device)
+        v = normal_chunked((total, hkv, d), gd, device)
+    else:
+        k = normal((total, hkv, d), torch.bfloat16, g)
+        v = normal((total, hkv, d), torch.bfloat16, g)
+    scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    return DecodeCase(q.to(device), k, v, cu.to(torch.int32), lens, scale)

@@ -274,3 +274,24 @@ def test_decode_cfg5_sampled(gpu_lib):
         el = float(np.max(np.abs(f64(lse[:, i:i + 1].cpu()) - rl)))
         assert e <= OUT_TOL and el <= LSE_TOL, (i, e, el)
     say("  sampled sequences within tolerance")
+
+
+def test_decode_split_kv_long_keys(gpu_lib):
+    """Few sequences with long keys: the split-KV (flash-decoding) path. Every
+    element against the oracle, an empty sequence gives out 0 / lse -inf, and a
+    q row of no sequence is left untouched."""
+    lens = [3000, 9001, 17, 0, 5000, 12000]
+    case = inputs.long_decode(lens, hq=32, hkv=4, d=128, seed=7)
+    wl = W.DecodeWorkload(case)
+    n = len(lens)
+    # one extra q row beyond the last sequence: must keep its contents
+    q = torch.cat([wl.q, wl.q[:1]], dim=0)
+    out = torch.full((n + 1, 32, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((32, n + 1), 3.0, dtype=torch.float32, device="cuda")
+    L.block_fwd(q, wl.k, wl.v, wl.cu_q, wl.cu_k, 1, wl.max_k, case.scale, None, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = O.decode_forward(case.q, case.k, case.v, case.cu_k, case.scale)
+    say(f"decode split-KV: lens {lens}")
+    check("out", out[:n].cpu(), ro, OUT_TOL)
+    check_lse("lse", lse[:, :n].cpu(), rl)
+    assert torch.all(out[n].cpu() == 7.0) and torch.all(lse[:, n].cpu() == 3.0)
