@@ -567,6 +567,19 @@ attn_status attn_ulysses_reshard_lse(int32_t uly, int32_t to_heads, const float 
   return hip_check(timed("attn_reshard", s, [&] { return launch_lse_reshard(a, s); }), "lse reshard kernel");
 }
 
+attn_status attn_out_transpose(const attn_tensor *src, void *dst, void *stream) {
+  TRY(check_tensor(src, "src"));
+  if (!dst && src->n_tok > 0) return fail(ATTN_ERR_NULL, "dst is NULL");
+  if (src->n_tok >= ((int64_t)1 << 31) || src->n_head * src->head_dim >= ((int64_t)1 << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "sizes reach 2^31");
+  TransposeArgs a;
+  a.src = src->data; a.s_st = src->stride_tok; a.s_sh = src->stride_head; a.dst = dst;
+  a.esize = src->dtype == ATTN_F32 ? 4 : 2;
+  a.n = (int32_t)src->n_tok; a.h = (int32_t)src->n_head; a.d = (int32_t)src->head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_check(timed("attn_transpose", s, [&] { return launch_out_transpose(a, s); }), "transpose kernel");
+}
+
 attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
   TRY(check_tensor(dout, "dout"));
   TRY(check_tensor(out, "out"));

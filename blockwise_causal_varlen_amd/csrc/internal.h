@@ -158,6 +158,14 @@ struct LseReshardArgs {
   int32_t uly, to_heads, n_local, h_local;
 };
 hipError_t launch_lse_reshard(const LseReshardArgs &a, hipStream_t s);
+
+// [KVP] `tp_out`: dst[h, d, t] = src[t, h, d] (contiguous [H, D, n] destination).
+struct TransposeArgs {
+  const void *src; int64_t s_st, s_sh;  // elements
+  void *dst;
+  int32_t esize, n, h, d;
+};
+hipError_t launch_out_transpose(const TransposeArgs &a, hipStream_t s);
 hipError_t launch_diag_bwd(const DiagArgs &a, hipStream_t s);
 
 struct BwdArgs {

@@ -313,6 +313,40 @@ hipError_t launch_lse_reshard(const LseReshardArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Transposed output (AWS NKI "Attention KV-Parallel Segmented CTE", parameter
+// `tp_out`: the output as [heads, D, S]): dst[h, d, t] = src[t, h, d]. A
+// work-group moves a 64-token x 64-column tile of one head through LDS, so
+// both the reads (along d) and the writes (along t) are contiguous.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void out_transpose_kernel(TransposeArgs a) {
+  __shared__ T tile[64][64 + 1];
+  const int t0 = blockIdx.x * 64, d0 = blockIdx.y * 64, h = blockIdx.z;
+  const T *src = (const T *)a.src;
+  T *dst = (T *)a.dst;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // read rows t0 + ty + 4i, columns d0 + tx
+    const int t = t0 + ty + 4 * i, d = d0 + tx;
+    if (t < a.n && d < a.d) tile[ty + 4 * i][tx] = src[(int64_t)t * a.s_st + (int64_t)h * a.s_sh + d];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // write rows d0 + ty + 4i of head h, columns t0 + tx
+    const int d = d0 + ty + 4 * i, t = t0 + tx;
+    if (t < a.n && d < a.d) dst[((int64_t)h * a.d + d) * a.n + t] = tile[tx][ty + 4 * i];
+  }
+}
+
+hipError_t launch_out_transpose(const TransposeArgs &a, hipStream_t s) {
+  if (a.n == 0 || a.h == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.n + 63) / 64), (unsigned)((a.d + 63) / 64), (unsigned)a.h);
+  if (a.esize == 2) hipLaunchKernelGGL(out_transpose_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(out_transpose_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // R-way merge (AWS NKI "Attention KV-Parallel Segmented CTE", Background:
 // the partials of the ranks are combined by online softmax):
 //   lse = m + log(sum_i exp(lse_i - m)),  out = sum_i exp(lse_i - lse) out_i

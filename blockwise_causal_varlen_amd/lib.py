@@ -68,6 +68,7 @@ _SIGS = {
     "attn_bwd_delta": (C.c_int, [T, T, P, P]),
     "attn_merge_diag": (C.c_int, [T, T, T, F, T, P, T, P]),
     "attn_ulysses_reshard": (C.c_int, [I32, I32, T, T, P]),
+    "attn_out_transpose": (C.c_int, [T, P, P]),
     "attn_ulysses_reshard_lse": (C.c_int, [I32, I32, P, P, I64, I64, P]),
     "attn_diag_bwd": (C.c_int, [T, T, T, T, P, P, F, T, T, T, P]),
     "attn_block_bwd": (C.c_int, [T, T, T, T, T, P, P, P, P, I32, I32, I32, M, F, T, T, T, P, SZ, P]),
@@ -277,6 +278,15 @@ def merge_diag(q, k, v, scale, out, lse, final_out=None, stream=None):
     _call("attn_merge_diag", C.byref(desc(q)), C.byref(desc(k)), C.byref(desc(v)), float(scale), C.byref(desc(out)),
           lse.data_ptr(), C.byref(desc(final_out)) if final_out is not None else None, _stream(stream))
     return out, lse
+
+
+def out_transpose(src, dst=None, stream=None):
+    """attn_out_transpose: [n, H, D] -> contiguous [H, D, n]."""
+    n, h, d = src.shape
+    if dst is None:
+        dst = torch.empty(h, d, n, dtype=src.dtype, device=src.device)
+    _call("attn_out_transpose", C.byref(desc(src)), dst.data_ptr(), _stream(stream))
+    return dst
 
 
 def ulysses_reshard(srcs, dsts, to_heads, stream=None):

@@ -274,6 +274,15 @@ attn_status attn_ulysses_reshard_lse(int32_t uly, int32_t to_heads, const float 
                                      int64_t n_local, int64_t n_head, void *stream);
 
 /*
+ * attn_out_transpose -- the transposed output of [KVP] (`tp_out`: [heads, D, S]
+ * instead of [heads, S, D]): dst[h, d, t] = src[t, h, d].
+ *   src  [n, H, D] bf16 or f32 (any token / head strides, last dim contiguous)
+ *   dst  device pointer to a contiguous [H, D, n] array of src's dtype
+ * A pure copy (bit-exact).
+ */
+attn_status attn_out_transpose(const attn_tensor *src, void *dst, void *stream);
+
+/*
  * attn_bwd_delta -- delta[h, i] = sum_d dout[i,h,d] * out[i,h,d] (f32), the
  * row term of the softmax backward, computed from the MERGED out; it is the
  * same for every block of a schedule, so a schedule computes it once.

@@ -240,6 +240,10 @@ def test_kvp_small_full_and_contiguous(gpu_lib):
         say(f"kvp small interleave={interleave}")
         check("out", out.cpu(), ro, OUT_TOL)
         check_lse("lse", lse.cpu(), rl)
+        # the transposed output ([KVP] tp_out: [heads, D, S]) is a bit-exact copy
+        tp = L.out_transpose(out)
+        torch.cuda.synchronize()
+        assert torch.equal(tp.cpu(), out.permute(1, 2, 0).cpu())
 
 
 def test_decode_small_full(gpu_lib):
