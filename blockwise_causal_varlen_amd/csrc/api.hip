@@ -307,11 +307,29 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
   return fail(ATTN_ERR_INVALID, "unknown op %d", (int)op);
 }
 
-attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+}  // extern "C"
+
+namespace {
+
+// A block forward that works on a running state (acc f32 with the lse given
+// to block_fwd_impl), in the forward kernel's epilogue: merge (else the block
+// initialises the state); rows of the document halves in final_view (bit 0
+// front, bit 1 back) have their last update here and go to the out tensor.
+struct FusedMerge {
+  const attn_tensor *acc;
+  bool merge;
+  int32_t final_view;
+};
+
+bool can_fuse_merge(const attn_tensor *q, int32_t max_seqlen_q, const attn_mask *m) {
+  return q->dtype == ATTN_BF16 && max_seqlen_q != 1 && !(m && (m->seg_size > 0 || m->block_table));
+}
+
+attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
                            int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
                            const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+                           void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr) {
   Problem P;
   TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
   TRY(check_out(out, P, "out"));
@@ -324,6 +342,13 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
   if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (num_seqs == 0 || P.n_q == 0) return ok();
+
+  if (fm) {
+    if (P.decode || P.nseg > 0 || P.paged || q->dtype != ATTN_BF16)
+      return fail(ATTN_ERR_UNSUPPORTED, "a fused merge needs the bf16 tiled forward");
+    TRY(check_out(fm->acc, P, "acc"));
+    if (fm->acc->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "running out must be f32");
+  }
 
   if (P.decode) {
     DecodeArgs a;
@@ -348,10 +373,15 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
   SchedBufs sb = sched_carve(w, cap);
   w += align256(sched_bytes(cap));
   MaskDev md = mask_dev(mask);
-  TRY(hip_check(timed("attn_sched", s, [&] {
-                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM,
-                                         kFwdBN, 0, (int32_t)P.nseg, sb, s);
-                }), "scheduler"));
+  if (pre) {
+    if (pre->capacity != cap) return fail(ATTN_ERR_INVALID, "internal: schedule capacity differs");
+    sb = *pre;
+  } else {
+    TRY(hip_check(timed("attn_sched", s, [&] {
+                    return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM,
+                                           kFwdBN, 0, (int32_t)P.nseg, sb, s);
+                  }), "scheduler"));
+  }
   FwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v);
   a.dtype = q->dtype; a.head_dim = (int32_t)P.d; a.hq = (int32_t)P.hq; a.hkv = (int32_t)P.hkv;
@@ -367,6 +397,11 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
   a.n_q = P.n_q;
   a.sched = sb;
   a.grid_items = cap;
+  if (fm) {
+    a.acc = (float *)fm->acc->data; a.a_st = fm->acc->stride_tok; a.a_sh = fm->acc->stride_head;
+    a.merge = fm->merge ? 1 : 0;
+    a.final_view = fm->final_view;
+  }
   if (P.nseg > 0) {
     a.part_out = (float *)w;
     w += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
@@ -389,6 +424,19 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
     TRY(hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(mn, s); }), "segment merge"));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                           const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
+                           const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+  return block_fwd_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, mask, scale, out,
+                        lse, workspace, workspace_bytes, stream, nullptr);
 }
 
 attn_status attn_merge_out_lse(const attn_tensor *out, float *lse, const attn_tensor *block_out,
@@ -595,11 +643,22 @@ attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, floa
   return hip_check(timed("attn_delta", s, [&] { return launch_delta(a, s); }), "delta kernel");
 }
 
-attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+}  // extern "C"
+
+namespace {
+
+// Schedules and lse2 computed once by a driver for several block backwards.
+struct BwdPre {
+  SchedBufs sq, sk;
+  const float *lse2;
+};
+
+attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                            const attn_tensor *out, const float *lse, const float *delta, const int32_t *cu_seqlens_q,
                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            const attn_mask *mask, float scale, const attn_tensor *dq, const attn_tensor *dk,
-                           const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream) {
+                           const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream,
+                           const BwdPre *pre) {
   TRY(check_qkv(q, k, v));
   TRY(check_mask(mask));
   if (mask && (mask->block_table || mask->seg_size > 0))
@@ -630,37 +689,46 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
   TRY(check_ranges(q, k, v, mask, k->n_tok));
   if (dout->stride_tok >= (1 << 22)) return fail(ATTN_ERR_UNSUPPORTED, "a row stride of 2^22 elements or more");
-  const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, delta == nullptr);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int64_t capq = sched_capacity(q->n_tok, num_seqs, kBwdTile, 1);
+  const int64_t capk = sched_capacity(k->n_tok, num_seqs, kBwdTile, 1);
+  if (pre) {
+    if (!delta) return fail(ATTN_ERR_INVALID, "internal: precomputed schedules need delta");
+  } else {
+    const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, delta == nullptr);
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   hipStream_t s = (hipStream_t)stream;
   if (num_seqs == 0 || q->n_tok == 0 || k->n_tok == 0) return ok();
 
-  char *w = (char *)workspace;
-  const int64_t capq = sched_capacity(q->n_tok, num_seqs, kBwdTile, 1);
-  const int64_t capk = sched_capacity(k->n_tok, num_seqs, kBwdTile, 1);
-  SchedBufs sq = sched_carve(w, capq);
-  w += align256(sched_bytes(capq));
-  SchedBufs sk = sched_carve(w, capk);
-  w += align256(sched_bytes(capk));
-  float *lse2 = (float *)w;
-  w += align256((size_t)q->n_head * q->n_tok * 4);
-  TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, s); }), "lse2"));
-  if (!delta) {
-    float *dl = (float *)w;
-    TRY(attn_bwd_delta(dout, out, dl, stream));
-    delta = dl;
-  }
   MaskDev md = mask_dev(mask);
-  TRY(hip_check(timed("attn_sched", s, [&] {
-                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN,
-                                         0, 1, sq, s);
-                }), "scheduler"));
-  TRY(hip_check(timed("attn_sched", s, [&] {
-                  return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ,
-                                         1, 1, sk, s);
-                }), "scheduler"));
+  SchedBufs sq, sk;
+  const float *lse2;
+  if (pre) {
+    if (pre->sq.capacity != capq || pre->sk.capacity != capk)
+      return fail(ATTN_ERR_INVALID, "internal: schedule capacity differs");
+    sq = pre->sq; sk = pre->sk; lse2 = pre->lse2;
+  } else {
+    char *w = (char *)workspace;
+    sq = sched_carve(w, capq);
+    w += align256(sched_bytes(capq));
+    sk = sched_carve(w, capk);
+    w += align256(sched_bytes(capk));
+    float *l2 = (float *)w;
+    w += align256((size_t)q->n_head * q->n_tok * 4);
+    TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, l2, q->n_head * q->n_tok, s); }), "lse2"));
+    lse2 = l2;
+    if (!delta) {
+      float *dl = (float *)w;
+      TRY(attn_bwd_delta(dout, out, dl, stream));
+      delta = dl;
+    }
+    const SchedJob jobs[2] = {
+        {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN, 0, 1, sq},
+        {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ, 1, 1, sk}};
+    TRY(hip_check(timed("attn_sched", s, [&] { return launch_schedules(jobs, 2, s); }), "scheduler"));
+  }
   BwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v); a.dout = tdev(dout);
   a.dtype = q->dtype; a.head_dim = (int32_t)q->head_dim; a.hq = (int32_t)q->n_head; a.hkv = (int32_t)k->n_head;
@@ -671,6 +739,19 @@ attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const 
   a.qsched = sq; a.ksched = sk; a.q_items = capq; a.k_items = capk;
   TRY(hip_check(timed("attn_dkdv", s, [&] { return launch_bwd(a, 0, s); }), "dK/dV kernel"));
   return hip_check(timed("attn_dq", s, [&] { return launch_bwd(a, 1, s); }), "dQ kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_block_bwd(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                           const attn_tensor *out, const float *lse, const float *delta, const int32_t *cu_seqlens_q,
+                           const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           const attn_mask *mask, float scale, const attn_tensor *dq, const attn_tensor *dk,
+                           const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream) {
+  return block_bwd_impl(dout, q, k, v, out, lse, delta, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
+                        max_seqlen_k, mask, scale, dq, dk, dv, workspace, workspace_bytes, stream, nullptr);
 }
 
 attn_status attn_zigzag_shard(const attn_tensor *src, const int32_t *cu_seqlens_global, int32_t num_seqs,
@@ -717,21 +798,57 @@ attn_mask zigzag_mask(int cp, int r, int s) {
   return make_mask(0, ATTN_VIEW_BACK, ATTN_VIEW_ALL);
 }
 
+// The distinct block kinds (masks) of a ring schedule: at most three (the
+// diagonal block, and one or two off-diagonal kinds), so the schedules of all
+// steps are computed up front, in one launch.
+constexpr int kRingKinds = 3;
+
 struct RingLayout {
-  size_t bout_off, blse_off, fwd_off, total;
+  size_t bout_off, blse_off, fwd_off, fsched_off, total;  // forward
+  size_t delta_off, lse2_off, bsched_off, btotal;           // backward
+  int64_t fcap, qcap, kcap;
+  size_t fsched_stride, bsched_stride;
 };
 
-RingLayout ring_layout(const attn_tensor *q, const attn_tensor *k, int32_t num_seqs, int32_t max_local) {
+RingLayout ring_layout(const attn_tensor *q, const attn_tensor *k, int32_t num_seqs) {
   Problem P;
   P.n_q = q->n_tok; P.hq = q->n_head; P.hkv = k->n_head; P.d = q->head_dim; P.nseg = 0; P.decode = false;
   P.paged = false; P.n_k_logical = k->n_tok;
-  (void)max_local;
   RingLayout L;
   L.bout_off = 0;
   L.blse_off = align256((size_t)q->n_tok * q->n_head * q->head_dim * esize(q->dtype));
   L.fwd_off = L.blse_off + align256((size_t)q->n_head * q->n_tok * 4);
-  L.total = L.fwd_off + fwd_ws_bytes(P, num_seqs);
+  L.fsched_off = L.fwd_off + fwd_ws_bytes(P, num_seqs);
+  L.fcap = sched_capacity(q->n_tok, num_seqs, kFwdBM, 0);
+  L.fsched_stride = align256(sched_bytes(L.fcap));
+  L.total = L.fsched_off + kRingKinds * L.fsched_stride;
+  L.qcap = sched_capacity(q->n_tok, num_seqs, kBwdTile, 1);
+  L.kcap = sched_capacity(k->n_tok, num_seqs, kBwdTile, 1);
+  L.bsched_stride = align256(sched_bytes(L.qcap)) + align256(sched_bytes(L.kcap));
+  L.delta_off = 0;
+  L.lse2_off = align256((size_t)q->n_head * q->n_tok * 4);
+  L.bsched_off = 2 * L.lse2_off;
+  L.btotal = L.bsched_off + kRingKinds * L.bsched_stride;
   return L;
+}
+
+// Masks of steps 0..n_steps-1 and the kind (index of the first equal mask) of each.
+attn_status ring_kinds(int32_t cp, int32_t rank, int32_t n_steps, attn_mask (*mk)(int, int, int),
+                       std::vector<attn_mask> &masks, std::vector<int> &kind_of, std::vector<attn_mask> &kinds) {
+  masks.resize(n_steps);
+  kind_of.resize(n_steps);
+  kinds.clear();
+  for (int s = 0; s < n_steps; ++s) {
+    masks[s] = mk(cp, rank, s);
+    int k = 0;
+    while (k < (int)kinds.size() && memcmp(&kinds[k], &masks[s], sizeof(attn_mask))) ++k;
+    if (k == (int)kinds.size()) {
+      if (k == kRingKinds) return fail(ATTN_ERR_INVALID, "internal: more than %d block kinds", kRingKinds);
+      kinds.push_back(masks[s]);
+    }
+    kind_of[s] = k;
+  }
+  return ok();
 }
 
 typedef attn_mask (*StepMask)(int cp, int r, int s);
@@ -760,8 +877,11 @@ attn_status run_ring_fwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   TRY(check_tensor(out_acc, "out_acc"));
   if (out_acc->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "out_acc must be f32");
   TRY(check_tensor(out, "out"));
-  RingLayout L = ring_layout(q, &k_loc[0], num_seqs, max_local);
+  if (num_seqs < 0 || max_local < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
+  if (num_seqs > 0 && !cu) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  RingLayout L = ring_layout(q, &k_loc[0], num_seqs);
   if (!ws || ws_bytes < L.total) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", L.total);
+  if (((uintptr_t)ws) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   char *w = (char *)ws;
   attn_tensor bout = *q;
   bout.data = w + L.bout_off;
@@ -769,20 +889,57 @@ attn_status run_ring_fwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   bout.stride_tok = q->n_head * q->head_dim;
   float *blse = (float *)(w + L.blse_off);
   void *fws = w + L.fwd_off;
-  const size_t fws_bytes = L.total - L.fwd_off;
+  const size_t fws_bytes = L.fsched_off - L.fwd_off;
+  Problem shp;
+  shp.n_q = q->n_tok; shp.hq = q->n_head; shp.d = q->head_dim;
+  TRY(check_out(out_acc, shp, "out_acc"));
+  hipStream_t st = (hipStream_t)stream;
+  // bf16: every block works on the running state in the forward's epilogue
+  const bool fuse = can_fuse_merge(q, max_local, nullptr);
+  // the tiled forward's schedules of every block kind, in one launch (the
+  // one-query decode path needs none)
+  std::vector<attn_mask> masks, kinds;
+  std::vector<int> kind_of;
+  TRY(ring_kinds(cp, rank, n_steps, mk, masks, kind_of, kinds));
+  std::vector<SchedBufs> sch(kinds.size());
+  const bool presched = max_local != 1 && num_seqs > 0 && q->n_tok > 0;
+  if (presched) {
+    SchedJob jobs[kRingKinds];
+    for (size_t i = 0; i < kinds.size(); ++i) {
+      TRY(check_mask(&kinds[i]));
+      sch[i] = sched_carve(w + L.fsched_off + i * L.fsched_stride, L.fcap);
+      jobs[i] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, mask_dev(&kinds[i]), kFwdBM, kFwdBN, 0, 1, sch[i]};
+    }
+    TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs, (int)kinds.size(), st); }),
+                  "scheduler"));
+  }
+  // the last step that updates each half of the documents' rows: there the
+  // fused epilogue writes the final output of that half
+  int last_front = -1, last_back = -1;
+  for (int s = 0; s < n_steps; ++s) {
+    if (masks[s].q_view != ATTN_VIEW_BACK) last_front = s;
+    if (masks[s].q_view != ATTN_VIEW_FRONT) last_back = s;
+  }
   for (int s = 0; s < n_steps; ++s) {
     const int src = ((rank - s) % cp + cp) % cp;
-    attn_mask m = mk(cp, rank, s);
+    const attn_mask &m = masks[s];
+    const SchedBufs *pre = presched ? &sch[kind_of[s]] : nullptr;
     const bool last = s == n_steps - 1;
+    if (fuse) {
+      const FusedMerge fm{out_acc, s > 0, (s == last_front ? 1 : 0) | (s == last_back ? 2 : 0)};
+      TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, out, lse,
+                         fws, fws_bytes, stream, &fm, pre));
+      continue;
+    }
     if (s == 0) {
       // the first block initialises the running state
       const attn_tensor *dst = (n_steps == 1) ? out : out_acc;
-      TRY(attn_block_fwd(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, dst, lse,
-                         fws, fws_bytes, stream));
+      TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, dst, lse,
+                         fws, fws_bytes, stream, nullptr, pre));
       continue;
     }
-    TRY(attn_block_fwd(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, &bout, blse,
-                       fws, fws_bytes, stream));
+    TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, &bout, blse,
+                       fws, fws_bytes, stream, nullptr, pre));
     TRY(attn_merge_out_lse(out_acc, lse, &bout, blse, cu, num_seqs, m.q_view, nullptr, last ? out : nullptr, 0,
                            stream));
   }
@@ -797,16 +954,41 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   TRY(check_ring_args(cp, rank, q, k_loc, v_loc));
   if (!dk_loc || !dv_loc) return fail(ATTN_ERR_NULL, "dk_loc/dv_loc is NULL");
   TRY(check_tensor(out, "out"));
-  const size_t dbytes = align256((size_t)q->n_head * q->n_tok * 4);
-  const size_t bneed = bwd_ws_bytes(q->n_tok, k_loc[0].n_tok, q->n_head, num_seqs, false);
-  if (!ws || ws_bytes < dbytes + bneed) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", dbytes + bneed);
-  float *delta = (float *)ws;
+  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (num_seqs < 0 || max_local < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
+  if (num_seqs > 0 && !cu) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+  const RingLayout L = ring_layout(q, &k_loc[0], num_seqs);
+  if (!ws || ws_bytes < L.btotal) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", L.btotal);
+  if (((uintptr_t)ws) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  char *w = (char *)ws;
+  float *delta = (float *)(w + L.delta_off);
+  float *lse2 = (float *)(w + L.lse2_off);
   TRY(attn_bwd_delta(dout, out, delta, stream));
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<attn_mask> masks, kinds;
+  std::vector<int> kind_of;
+  TRY(ring_kinds(cp, rank, n_steps, mk, masks, kind_of, kinds));
+  std::vector<BwdPre> pre(kinds.size());
+  if (num_seqs > 0 && q->n_tok > 0) {
+    TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st); }), "lse2"));
+    SchedJob jobs[2 * kRingKinds];
+    for (size_t i = 0; i < kinds.size(); ++i) {
+      TRY(check_mask(&kinds[i]));
+      char *b = w + L.bsched_off + i * L.bsched_stride;
+      pre[i].sq = sched_carve(b, L.qcap);
+      pre[i].sk = sched_carve(b + align256(sched_bytes(L.qcap)), L.kcap);
+      pre[i].lse2 = lse2;
+      const MaskDev md = mask_dev(&kinds[i]);
+      jobs[2 * i] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kFwdBN, 0, 1, pre[i].sq};
+      jobs[2 * i + 1] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kBwdBQ, 1, 1, pre[i].sk};
+    }
+    TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs, 2 * (int)kinds.size(), st); }),
+                  "scheduler"));
+  }
   for (int s = 0; s < n_steps; ++s) {
     const int src = ((rank - s) % cp + cp) % cp;
-    attn_mask m = mk(cp, rank, s);
-    TRY(attn_block_bwd(dout, q, &k_loc[src], &v_loc[src], out, lse, delta, cu, cu, num_seqs, max_local, max_local,
-                       &m, scale, dq, &dk_loc[src], &dv_loc[src], (char *)ws + dbytes, ws_bytes - dbytes, stream));
+    TRY(block_bwd_impl(dout, q, &k_loc[src], &v_loc[src], out, lse, delta, cu, cu, num_seqs, max_local, max_local,
+                       &masks[s], scale, dq, &dk_loc[src], &dv_loc[src], nullptr, 0, stream, &pre[kind_of[s]]));
   }
   return ok();
 }
@@ -819,9 +1001,9 @@ attn_status attn_zigzag_workspace_size(int32_t cp, const attn_tensor *q, const a
   if (cp < 1) return fail(ATTN_ERR_INVALID, "cp must be >= 1");
   TRY(check_tensor(q, "q"));
   TRY(check_tensor(k, "k"));
-  const size_t f = ring_layout(q, k, num_seqs, max_seqlen_local).total;
-  const size_t b = align256((size_t)q->n_head * q->n_tok * 4) + bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, false);
-  *bytes = f > b ? f : b;
+  (void)max_seqlen_local;
+  const RingLayout L = ring_layout(q, k, num_seqs);
+  *bytes = L.total > L.btotal ? L.total : L.btotal;
   return ok();
 }
 

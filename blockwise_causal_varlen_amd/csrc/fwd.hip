@@ -53,16 +53,7 @@ int64_t sched_capacity(int64_t n_rows, int32_t num_seqs, int32_t tile, int64_t n
   return (n_rows / tile + num_seqs + 1) * (n_seg > 0 ? n_seg : 1);
 }
 
-struct SchedParams {
-  const int32_t *cu_q, *cu_k;
-  int32_t num_seqs;
-  int64_t n_q, n_k;
-  MaskDev m;
-  int32_t tile, key_tile;
-  int32_t by_keys;  // 0: tiles of query rows; 1: tiles of key rows (dK/dV)
-  int32_t max_seg;  // segments the partial buffers hold (longer documents are cut)
-  SchedBufs sb;
-};
+using SchedParams = SchedJob;
 
 __device__ __forceinline__ void view_range(int64_t s, int64_t e, int view, int64_t &a, int64_t &b) {
   int64_t h = (e - s) / 2;
@@ -99,6 +90,7 @@ __device__ void make_item(const SchedParams &p, int64_t qs, int64_t qe, int64_t 
   view_range(ks, ke, m.k_view, ka, kb);
   const int64_t nk_doc = ke - ks;
   it.qdoc0 = (int32_t)qs;
+  it.qmid = (int32_t)(qs + (qe - qs) / 2);
   it.kdoc0 = (int32_t)ks;
   it.seg = (int32_t)sg;
   if (p.by_keys) {
@@ -143,7 +135,7 @@ __device__ void make_item(const SchedParams &p, int64_t qs, int64_t qe, int64_t 
   it.cost = (int32_t)((hi - lo + p.key_tile - 1) / p.key_tile + 1);
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
+__device__ void sched_run(const SchedParams &p) {
   __shared__ int32_t s_buf[kSchedThreads];
   __shared__ int32_t s_base[kSchedThreads + 1];  // first item of each doc in the chunk
   __shared__ int32_t s_nseg[kSchedThreads];
@@ -221,11 +213,30 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) {
   if (tid == 0) *p.sb.count = count;
 }
 
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedParams p) { sched_run(p); }
+
+// several independent schedules, one workgroup each
+struct SchedBatch {
+  SchedParams p[kMaxSchedJobs];
+};
+__global__ __launch_bounds__(kSchedThreads) void sched_batch_kernel(SchedBatch b) { sched_run(b.p[blockIdx.x]); }
+
 hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs, int64_t n_q,
                            int64_t n_k, const MaskDev &m, int32_t tile, int32_t key_tile,
                            int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s) {
   SchedParams p{cu_q, cu_k, num_seqs, n_q, n_k, m, tile, key_tile, by_keys, max_seg < 1 ? 1 : max_seg, sb};
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedules(const SchedJob *jobs, int n, hipStream_t s) {
+  if (n < 1 || n > kMaxSchedJobs) return hipErrorInvalidValue;
+  SchedBatch b{};
+  for (int i = 0; i < n; ++i) {
+    b.p[i] = jobs[i];
+    if (b.p[i].max_seg < 1) b.p[i].max_seg = 1;
+  }
+  hipLaunchKernelGGL(sched_batch_kernel, dim3((unsigned)n), dim3(kSchedThreads), 0, s, b);
   return hipGetLastError();
 }
 
@@ -247,6 +258,9 @@ struct FwdParams {
   float *part_out, *part_lse;
   int64_t n_q;
   const WorkItem *items; const int32_t *order; const int32_t *count;
+  // running state (acc, lse) when acc is set: see FwdArgs
+  float *acc; int64_t a_st, a_sh;
+  int32_t merge, final_view;
 };
 
 template <typename T> struct Tile;  // LDS pitches (elements)
@@ -777,22 +791,50 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
     return;
   }
   OutT *orow = (OutT *)p.out + (int64_t)row * p.o_st + (int64_t)h * p.o_sh;
+  float wa = 0.f, wb = inv;  // output = wa * acc + wb * (unnormalised o)
+  float *arow = p.acc + (int64_t)row * p.a_st + (int64_t)h * p.a_sh;
+  const int64_t lidx = (int64_t)h * p.lse_n + row;
+  float ln = lse_v;
+  if (p.merge) {
+    // online-softmax merge with the running state of this (row, head), in the
+    // sigmoid form: lse' = max + log1p(exp(-|la - lb|)), sig = exp(lb - lse'),
+    // out' = acc - sig (acc - block_out); an empty side has weight 0
+    const float la = p.lse[lidx], lb = lse_v;
+    if (fmaxf(la, lb) == neg_inf()) {
+      ln = neg_inf(); wb = 0.f;
+    } else if (la == neg_inf()) {
+      ln = lb;
+    } else if (lb == neg_inf()) {
+      ln = la; wa = 1.f; wb = 0.f;
+    } else {
+      ln = fmaxf(la, lb) + log1pf(expf(-fabsf(la - lb)));
+      const float sig = expf(lb - ln);
+      wa = 1.f - sig; wb = sig * inv;
+    }
+  }
+  if (g == 0) p.lse[lidx] = ln;  // after every lane's read: ln depends on it
+  // rows whose result is final go to out, the others to the running acc
+  const bool fin = p.acc == nullptr || ((row < it.qmid ? 1 : 2) & p.final_view);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      if constexpr (sizeof(OutT) == 4) {
-        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
+      float4 v4 = {o[dt][4 * j4] * wb, o[dt][4 * j4 + 1] * wb, o[dt][4 * j4 + 2] * wb, o[dt][4 * j4 + 3] * wb};
+      if (wa != 0.f) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(arow + d0);
+        v4.x += wa * a4.x; v4.y += wa * a4.y; v4.z += wa * a4.z; v4.w += wa * a4.w;
+      }
+      if (!fin) {
+        *reinterpret_cast<float4 *>(arow + d0) = v4;
+      } else if constexpr (sizeof(OutT) == 4) {
         *reinterpret_cast<float4 *>(orow + d0) = v4;
       } else {
-        bf16x4 v4;
-        v4[0] = (bf16)(o[dt][4 * j4] * inv); v4[1] = (bf16)(o[dt][4 * j4 + 1] * inv);
-        v4[2] = (bf16)(o[dt][4 * j4 + 2] * inv); v4[3] = (bf16)(o[dt][4 * j4 + 3] * inv);
-        *reinterpret_cast<bf16x4 *>(orow + d0) = v4;
+        bf16x4 b4;
+        b4[0] = (bf16)v4.x; b4[1] = (bf16)v4.y; b4[2] = (bf16)v4.z; b4[3] = (bf16)v4.w;
+        *reinterpret_cast<bf16x4 *>(orow + d0) = b4;
       }
     }
-  if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
 }
 
 template <typename T, int D>
@@ -830,6 +872,8 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   fp.part_out = a.part_out; fp.part_lse = a.part_lse;
   fp.n_q = a.n_q;
   fp.items = a.sched.items; fp.order = a.sched.order; fp.count = a.sched.count;
+  fp.acc = a.acc; fp.a_st = a.a_st; fp.a_sh = a.a_sh;
+  fp.merge = a.acc != nullptr && a.merge; fp.final_view = a.final_view;
   const int64_t grid = a.grid_items * a.hq;
   if (grid <= 0) return hipSuccess;
   if (a.dtype == 0) {

@@ -19,6 +19,7 @@ struct WorkItem {
   int32_t kdoc0;       // first key row of the document
   int32_t seg;         // segment index (0 when not segmented)
   int32_t cost;        // key tiles + 1, the sort key
+  int32_t qmid;        // first row of the document's back half
 };
 
 // Device view of the visibility rule.
@@ -53,6 +54,21 @@ size_t sched_bytes(int64_t capacity);
 SchedBufs sched_carve(void *ws, int64_t capacity);
 int64_t sched_capacity(int64_t n_rows_view_bound, int32_t num_seqs, int32_t tile, int64_t n_seg);
 
+// One schedule: the work items of a (cu_q, cu_k, mask) problem, sorted by cost.
+struct SchedJob {
+  const int32_t *cu_q, *cu_k;
+  int32_t num_seqs;
+  int64_t n_q, n_k;
+  MaskDev m;
+  int32_t tile, key_tile;
+  int32_t by_keys;  // 0: tiles of query rows; 1: tiles of key rows (dK/dV)
+  int32_t max_seg;  // segments the partial buffers hold (longer documents are cut)
+  SchedBufs sb;
+};
+constexpr int kMaxSchedJobs = 8;
+// n (<= kMaxSchedJobs) independent schedules in one launch
+hipError_t launch_schedules(const SchedJob *jobs, int n, hipStream_t s);
+
 hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs,
                            int64_t n_q, int64_t n_k, const MaskDev &m, int32_t tile,
                            int32_t key_tile, int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s);
@@ -75,6 +91,12 @@ struct FwdArgs {
   int64_t n_q;
   SchedBufs sched;
   int64_t grid_items;           // scheduler capacity (grid bound)
+  // Running-state mode (bf16 tiled forward only), when acc is set: `lse` is
+  // the running lse; merge: combine the block with (acc, lse) first (else the
+  // block initialises them); rows of the halves in final_view (bit 0 front,
+  // bit 1 back) go to `out`, the others to acc (f32)
+  float *acc = nullptr; int64_t a_st = 0, a_sh = 0;
+  int32_t merge = 0, final_view = 0;
 };
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s);
 

@@ -45,52 +45,94 @@ __device__ __forceinline__ bool row_in_view(const int32_t *cu, int32_t num_seqs,
   return view == 1 ? row < s + h : row >= s + h;
 }
 
+// One workgroup streams one row (all heads) at a time; the view test is one
+// (uniform) binary search per row. Per pass a group of D/4 lanes owns one
+// head (16 bytes a lane); NB passes' loads are issued before any is used.
 template <int D, typename BT, typename FT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int G = D / 4;  // lanes per (row, head)
-  const int64_t total = a.n * a.h;
-  const int sub = threadIdx.x % G;
-  const int64_t per_blk = 256 / G;
-  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
-    const int64_t row = pr / a.h;
-    const int64_t h = pr - row * a.h;
-    const int64_t li = h * a.n + row;
-    if (!row_in_view(a.cu, a.num_seqs, a.view, row)) {
+  constexpr int G = D / 4;      // lanes per (row, head)
+  constexpr int HP = 256 / G;   // heads per pass
+  constexpr int NB = 2;         // passes in flight (more measured slower)
+  const int sub = threadIdx.x % G, hl = threadIdx.x / G;
+  const int H = (int)a.h;
+  for (int64_t row = blockIdx.x; row < a.n; row += gridDim.x) {
+    const bool in_view = row_in_view(a.cu, a.num_seqs, a.view, row);
+    const float *orow = a.out + row * a.o_st + 4 * sub;
+    if (!in_view) {
       // rows outside the view keep their state; a final cast still covers them
-      if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub,
-                          ld4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub));
+      if (!a.fout) continue;
+      FT *frow = (FT *)a.fout + row * a.f_st + 4 * sub;
+      for (int hb = 0; hb < H; hb += NB * HP) {
+        f32x4 v[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const int h = hb + k * HP + hl;
+          if (h < H) v[k] = ld4<float>(orow + h * a.o_sh);
+        }
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+          const int h = hb + k * HP + hl;
+          if (h < H) st4<FT>(frow + h * a.f_sh, v[k]);
+        }
+      }
       continue;
     }
-    const float lb = a.blse[li];
-    const f32x4 bo = ld4<BT>((const BT *)a.bout + row * a.b_st + h * a.b_sh + 4 * sub);
-    float ln, sig;
-    f32x4 res;
-    if (a.init) {
-      ln = lb; sig = 1.f; res = bo;
-    } else {
-      const float la = a.lse[li];
-      const f32x4 oa = ld4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub);
-      const float mx = fmaxf(la, lb);
-      // an empty partial (lse = -inf) has weight 0, whatever its out holds
-      if (mx == neg_inf()) {
-        ln = neg_inf(); sig = 0.f; res = f32x4{};
-      } else if (la == neg_inf()) {
-        ln = lb; sig = 1.f; res = bo;
-      } else if (lb == neg_inf()) {
-        ln = la; sig = 0.f; res = oa;
-      } else {
-        ln = mx + log1pf(expf(-fabsf(la - lb)));
-        sig = expf(lb - ln);
-        res = oa - sig * (oa - bo);
+    const BT *brow = (const BT *)a.bout + row * a.b_st + 4 * sub;
+    for (int hb = 0; hb < H; hb += NB * HP) {
+      f32x4 oa[NB], bo[NB];
+      float la[NB], lb[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int h = hb + k * HP + hl;
+        if (h < H) {
+          const int64_t li = (int64_t)h * a.n + row;
+          lb[k] = a.blse[li];
+          bo[k] = ld4<BT>(brow + h * a.b_sh);
+          if (!a.init) {
+            la[k] = a.lse[li];
+            oa[k] = ld4<float>(orow + h * a.o_sh);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int h = hb + k * HP + hl;
+        if (h >= H) continue;
+        float ln, sig;
+        f32x4 res;
+        if (a.init) {
+          ln = lb[k]; sig = 1.f; res = bo[k];
+        } else {
+          const float mx = fmaxf(la[k], lb[k]);
+          // an empty partial (lse = -inf) has weight 0, whatever its out holds
+          if (mx == neg_inf()) {
+            ln = neg_inf(); sig = 0.f; res = f32x4{};
+          } else if (la[k] == neg_inf()) {
+            ln = lb[k]; sig = 1.f; res = bo[k];
+          } else if (lb[k] == neg_inf()) {
+            ln = la[k]; sig = 0.f; res = oa[k];
+          } else {
+            ln = mx + log1pf(expf(-fabsf(la[k] - lb[k])));
+            sig = expf(lb[k] - ln);
+            res = oa[k] - sig * (oa[k] - bo[k]);
+          }
+        }
+        if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub, res);
+        else st4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub, res);
+        if (sub == 0) {
+          const int64_t li = (int64_t)h * a.n + row;
+          a.lse[li] = ln;
+          if (a.weight) a.weight[li] = sig;
+        }
       }
     }
-    if (a.fout) st4<FT>((FT *)a.fout + row * a.f_st + h * a.f_sh + 4 * sub, res);
-    else st4<float>(a.out + row * a.o_st + h * a.o_sh + 4 * sub, res);
-    if (sub == 0) {
-      a.lse[li] = ln;
-      if (a.weight) a.weight[li] = sig;
-    }
   }
+}
+
+// workgroups of a row-streaming kernel: one per row up to 16 per CU
+static unsigned row_grid(int64_t rows) {
+  const int64_t cap = 256 * 16;
+  return (unsigned)(rows < 1 ? 1 : (rows > cap ? cap : rows));
 }
 
 static unsigned stream_grid(int64_t pairs, int per_blk) {
@@ -110,7 +152,7 @@ static void launch_merge_b(const MergeArgs &a, hipStream_t s, unsigned grid) {
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s) {
   if (a.n * a.h == 0) return hipSuccess;
-  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  const unsigned grid = row_grid(a.n);
   if (a.d == 128) {
     if (a.bout_dtype == 0) launch_merge_b<128, bf16>(a, s, grid);
     else launch_merge_b<128, float>(a, s, grid);
@@ -408,21 +450,51 @@ hipError_t launch_merge_n(const MergeNArgs &a, hipStream_t s) {
 // every block's backward sees the final merged out, so this row term is the
 // same for all blocks and is computed once).
 // ---------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ void ld8(const T *p, float (&v)[8]);
+template <> __device__ __forceinline__ void ld8<bf16>(const bf16 *p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+template <> __device__ __forceinline__ void ld8<float>(const float *p, float (&v)[8]) {
+  const f32x4 x = *reinterpret_cast<const f32x4 *>(p), y = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = x[i]; v[4 + i] = y[i]; }
+}
+
+// One workgroup streams one row (all heads) at a time; a group of D/8 lanes
+// owns one head (8 elements a lane), NB passes' loads in flight.
 template <int D, typename T1, typename T2>
 __global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
-  constexpr int G = D / 4;
-  const int64_t total = a.n * a.h;
-  const int sub = threadIdx.x % G;
-  const int64_t per_blk = 256 / G;
-  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
-    const int64_t row = pr / a.h;
-    const int64_t h = pr - row * a.h;
-    const f32x4 x = ld4<T1>((const T1 *)a.dout + row * a.do_st + h * a.do_sh + 4 * sub);
-    const f32x4 y = ld4<T2>((const T2 *)a.out + row * a.o_st + h * a.o_sh + 4 * sub);
-    float v = x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+  constexpr int G = D / 8;
+  constexpr int HP = 256 / G;
+  constexpr int NB = 2;
+  const int sub = threadIdx.x % G, hl = threadIdx.x / G;
+  const int H = (int)a.h;
+  for (int64_t row = blockIdx.x; row < a.n; row += gridDim.x) {
+    const T1 *xr = (const T1 *)a.dout + row * a.do_st + 8 * sub;
+    const T2 *yr = (const T2 *)a.out + row * a.o_st + 8 * sub;
+    for (int hb = 0; hb < H; hb += NB * HP) {
+      float x[NB][8] = {}, y[NB][8] = {};
 #pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (sub == 0) a.delta[h * a.n + row] = v;
+      for (int k = 0; k < NB; ++k) {
+        const int h = hb + k * HP + hl;
+        if (h < H) {
+          ld8<T1>(xr + h * a.do_sh, x[k]);
+          ld8<T2>(yr + h * a.o_sh, y[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int h = hb + k * HP + hl;
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v = __builtin_fmaf(x[k][i], y[k][i], v);
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (h < H && sub == 0) a.delta[(int64_t)h * a.n + row] = v;
+      }
+    }
   }
 }
 
@@ -436,7 +508,7 @@ static void launch_delta_d(const DeltaArgs &a, hipStream_t s, unsigned grid) {
 
 hipError_t launch_delta(const DeltaArgs &a, hipStream_t s) {
   if (a.n * a.h == 0) return hipSuccess;
-  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  const unsigned grid = row_grid(a.n);
   if (a.d == 128) launch_delta_d<128>(a, s, grid);
   else launch_delta_d<64>(a, s, grid);
   return hipGetLastError();
