@@ -189,33 +189,19 @@ def headline(args, torch, lib, I, W):
     pairs = wl.pairs_per_rank()
     fwd_f, bwd_f = 4 * d * hq * pairs, 10 * d * hq * pairs
     tflops = (fwd_f + bwd_f) / sec / 1e12
-    # algorithmic bytes of the merges: (row, head) units per step, 1292 B each
-    # (f32 out read+write 1024, bf16 block out 256, lse 3 x 4) except the last,
-    # fused with the bf16 cast (view rows 1036 B, other rows 768 B)
     doc_lens = wl.doc_lens
     rows_all = sum(L_ // cp for L_ in doc_lens)
-    rows_back = sum(L_ // (2 * cp) for L_ in doc_lens)
-    merge_units = []
-    for s in range(1, cp):
-        view_rows = rows_all if s <= r else rows_back
-        last = s == cp - 1
-        b = view_rows * hq * (1036 if last else 1292)
-        if last:
-            b += (rows_all - view_rows) * hq * 768
-        merge_units.append(b)
-    merge_bytes = sum(merge_units)
     delta_bytes = rows_all * hq * (256 + 256 + 4)
     kernels = {
         "attn_fwd": roofline("attn_fwd", fwd_f, kt, args.steps, "mfma", load_traffic("attn_fwd")),
         "attn_dkdv": roofline("attn_dkdv", 8 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dkdv")),
         "attn_dq": roofline("attn_dq", 2 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dq")),
-        "attn_merge": roofline("attn_merge", merge_bytes, kt, args.steps, "hbm", load_traffic("attn_merge")),
         "attn_delta": roofline("attn_delta", delta_bytes, kt, args.steps, "hbm", load_traffic("attn_delta")),
     }
     times = {k: v[1] for k, v in kt.items()}
     dominant = max((k for k in kernels if kernels[k]), key=lambda k: times.get(k, 0.0))
-    cfg = {"workload": "zigzag cp=8, virtual rank 3 of 131072 packed tokens (16384 local rows), fwd 8 blocks + "
-                       "7 merges + bwd (delta + 8 merged-lse blocks)",
+    cfg = {"workload": "zigzag cp=8, virtual rank 3 of 131072 packed tokens (16384 local rows), fwd 8 blocks "
+                       "(7 merges in the forward epilogue) + bwd (delta + 8 merged-lse blocks)",
            "tokens_global": 131072, "local_rows": nloc, "docs": len(doc_lens), "hq": hq, "hkv": 8, "head_dim": d,
            "cp": cp, "rank": r, "visible_pairs_per_head": pairs,
            "flops_fwd": fwd_f, "flops_bwd": bwd_f, "parallelism": "one virtual rank on one GPU"}
@@ -293,6 +279,21 @@ def other_rows(args, torch, lib, I, W):
         "kernel_ms": kt}
     del wu, cu_case, full
     torch.cuda.empty_cache()
+    # the standalone merge kernel (one block into the running state) at the
+    # headline rank's shape: f32 state read + written, bf16 block out, lse
+    gm = torch.Generator(device="cuda")
+    gm.manual_seed(7)
+    n, hq, d = 16384, 32, 128
+    acc = torch.randn(n, hq, d, device="cuda", dtype=torch.float32, generator=gm)
+    lse = torch.randn(hq, n, device="cuda", dtype=torch.float32, generator=gm)
+    bo = torch.randn(n, hq, d, device="cuda", dtype=torch.float32, generator=gm).to(torch.bfloat16)
+    bl = torch.randn(hq, n, device="cuda", dtype=torch.float32, generator=gm)
+    sec, kt = timed_steps(lambda: lib.merge(acc, lse, bo, bl), steps, 1, torch, lib)
+    b = n * hq * (d * 4 * 2 + d * 2 + 12)
+    rows["merge_16384x32x128"] = {"ms": sec * 1e3, "GB/s": b / sec / 1e9, "frac": b / sec / 1e9 / PEAK_HBM_GBS,
+                                  "bytes": b, "merge_kernel": roofline("attn_merge", b, kt, steps, "hbm",
+                                                                       load_traffic("attn_merge"))}
+    del acc, lse, bo, bl
     c5 = I.cfg5(device="cuda")
     w5 = W.DecodeWorkload(c5)
     sec, kt = timed_steps(w5.forward, steps, 1, torch, lib)
