@@ -18,6 +18,8 @@
 //   * dQ: a workgroup owns 128 query rows of one q head (like the forward),
 //     keeps Q and dO in registers, stages K/V tiles, computes S^T = K Q^T and
 //     dP^T = V dO^T, and accumulates dQ^T += K^T dS^T (K^T by transpose read).
+#include <type_traits>
+
 #include "internal.h"
 
 namespace attn {
@@ -118,6 +120,31 @@ __device__ __forceinline__ void acc_transposed_all(f32x16 (&acc)[ND], const bf16
       i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + ra * pitch + col));
       i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(base + (ra + 8) * pitch + col));
       bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+      a[dt][0] = l4[0]; a[dt][1] = l4[1]; a[dt][2] = l4[2]; a[dt][3] = l4[3];
+      a[dt][4] = h4[0]; a[dt][5] = h4[1]; a[dt][6] = h4[2]; a[dt][7] = h4[3];
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) acc[dt] = Mfma32<bf16>::mma(a[dt], b, acc[dt]);
+  }
+}
+
+// acc_transposed_all on a SwzTile128 (offsets from swz_tr_offsets; r0 a
+// multiple of 16).
+template <int ND>
+__device__ __forceinline__ void acc_transposed_swz(f32x16 (&acc)[ND], const bf16 *base, int r0, const int (&lo)[ND],
+                                                   const int (&hi)[ND], const float (&pv)[16]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)pv[t * 8 + e];
+    const bf16 *blk = base + (r0 + t * 16) * 128;
+    bf16x8 a[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      i16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + lo[dt]));
+      i16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + hi[dt]));
+      bf16x4 l4 = __builtin_bit_cast(bf16x4, l), h4 = __builtin_bit_cast(bf16x4, h);
       a[dt][0] = l4[0]; a[dt][1] = l4[1]; a[dt][2] = l4[2]; a[dt][3] = l4[3];
       a[dt][4] = h4[0]; a[dt][5] = h4[1]; a[dt][6] = h4[2]; a[dt][7] = h4[3];
     }
@@ -382,7 +409,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   constexpr int ND = D / 32;
   constexpr int QB = kBwdBQ;
   static_assert(QB == 64, "tiles are 64 rows");
-  using QT = PadTile<D, D / 8 + 5>;  // row reads and transpose reads
+  // row reads and transpose reads: swizzled (D = 128) or padded (at most 2-way)
+  using QT = std::conditional_t<D == 128, SwzTile128, PadTile<D, D / 8 + 5>>;
   __shared__ __attribute__((aligned(1024))) bf16 sQ0[QT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sO0[QT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sQ1[QT::ELEMS];
@@ -441,6 +469,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   int qoffs[QT::NJ], ooffs[QT::NJ];
   tile_voffsets<QT>(qoffs, p.q_st, w, lane);
   tile_voffsets<QT>(ooffs, p.do_st, w, lane);
+  int ro[NS], trl[ND], trh[ND];  // swizzled tiles: per-lane read offsets
+  if constexpr (QT::kSwz) {
+    swz_row_offsets<NS>(ro, lane);
+    swz_tr_offsets<ND>(trl, trh, lane);
+  }
   const int32_t qst = (int32_t)p.q_st, ost = (int32_t)p.do_st;
   const int32_t nqt = (q1 - q0 + QB - 1) / QB;
   const int32_t total = p.group * nqt;
@@ -467,8 +500,115 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     advance(sh, sqt);
   };
 
-  // One 64-row query tile against the wave's 32 keys. Rows past the end of the
+  // A operand: rows sub*32 + l32 of a Q / dO tile, k-step st (d columns)
+  auto afrag = [&](const bf16 *t, int sub, int st) -> bf16x8 {
+    const int off = QT::kSwz ? sub * 32 * 128 + ro[st] : (sub * 32 + l32) * QT::PITCH + st * 16 + g * 8;
+    return *reinterpret_cast<const bf16x8 *>(t + off);
+  };
+  // transposed A operand: d rows dt*32.. of a tile, k = its rows r0 + 16 tt +
+  // c_row order (the lane's rows 4g + u/4 and 8 more)
+  const int u = lane & 15, dh = (lane >> 4) & 1;
+  auto trfrag = [&](const bf16 *t, int r0, int tt, int dt) -> bf16x8 {
+    const bf16 *lo_p, *hi_p;
+    if constexpr (QT::kSwz) {
+      const bf16 *blk = t + (r0 + tt * 16) * 128;
+      lo_p = blk + trl[dt];
+      hi_p = blk + trh[dt];
+    } else {
+      const int ra = r0 + tt * 16 + 4 * g + (u >> 2);
+      const int col = dt * 32 + dh * 16 + 4 * (u & 3);
+      lo_p = t + ra * QT::PITCH + col;
+      hi_p = t + (ra + 8) * QT::PITCH + col;
+    }
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo_p));
+    const bf16x4 h4 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi_p));
+    bf16x8 r;
+    r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
+    r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
+    return r;
+  };
+
+  // One 64-row query tile against the wave's 32 keys as one straight-line
+  // block of steps, each two MFMAs plus the reads and VALU work placed beside
+  // them (the order is pinned by scheduling fences):
+  //   score steps k = 0..2NS-1: S = Q K^T and dP = dO V^T of row half k / NS,
+  //     d-chunk k % NS; the A fragments are read PFA steps ahead; during the
+  //     second half's steps the first half's probabilities are formed;
+  //   gradient steps k = 0..4ND-1: dV^T += dO^T P and dK^T += Q^T dS of row
+  //     half k / 2ND, 16-row part (k / ND) % 2, d-tile k % ND, transpose reads
+  //     PFT steps ahead; during the first half's steps the second half's
+  //     probabilities are formed.
+  // The mask is branch free (a branch between a masked and an unmasked copy
+  // measured slower: the copies' register assignments differ and the joins
+  // cost moves): the lane's key is visible from row offset c iff
+  // mlo <= c < mlo + mspan (full tiles: every c). Rows past the end of the
   // range hold zeros in Q and dO (and in lse2 / delta), so they add nothing.
+  auto body = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd, int32_t mlo, uint32_t mspan) {
+    constexpr int KS = 2 * NS;      // score steps
+    constexpr int KG = 4 * ND;      // gradient steps
+    constexpr int PFA = 3, PFT = 3;  // read-ahead distances (steps)
+    constexpr int JS = 16 / NS;     // probabilities formed per step (both phases)
+    static_assert(16 % NS == 0 && 16 / (2 * ND) == JS, "two probability slots per step");
+    const float sl2 = p.scale_log2;
+    f32x16 sc[2] = {f32x16{}, f32x16{}}, dpv[2] = {f32x16{}, f32x16{}};
+    bf16x8 pb[2][2], db[2][2];  // [half][16-row part]: P and dS as bf16 B operands
+    f32x4 l4[2], d4[2];         // row terms of the current 4-row group, by half
+    // one probability (row c_row(j) of half sub): exp2(S scale log2e - lse2),
+    // masked; dS = P (dP - delta)
+    auto prob = [&](int sub, int j) {
+      if ((j & 3) == 0) {
+        const int q4 = sub * 32 + 8 * (j >> 2) + 4 * g;
+        l4[sub] = *reinterpret_cast<const f32x4 *>(sl + q4);
+        d4[sub] = *reinterpret_cast<const f32x4 *>(sd + q4);
+      }
+      const int e = j & 3;
+      const int c = sub * 32 + 8 * (j >> 2) + e;  // row offset from the lane's first row
+      float ex = fast_exp2(__builtin_fmaf(sc[sub][j], sl2, -l4[sub][e]));
+      ex = (uint32_t)(c - mlo) < mspan ? ex : 0.f;
+      pb[sub][j >> 3][j & 7] = (bf16)ex;
+      db[sub][j >> 3][j & 7] = (bf16)(ex * (dpv[sub][j] - d4[sub][e]));
+    };
+    bf16x8 fq[KS], fo[KS];  // A fragments by score step (each live for PFA steps)
+    auto load_a = [&](int k) {
+      fq[k] = afrag(sq, k / NS, k % NS);
+      fo[k] = afrag(so, k / NS, k % NS);
+    };
+    bf16x8 tq[KG], to[KG];  // transposed A fragments by gradient step
+    auto load_t = [&](int k) {
+      const int sub = k / (2 * ND), tt = (k / ND) % 2, dt = k % ND;
+      to[k] = trfrag(so, sub * 32, tt, dt);
+      tq[k] = trfrag(sq, sub * 32, tt, dt);
+    };
+#pragma unroll
+    for (int k = 0; k < PFA; ++k) load_a(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      if (k + PFA < KS) load_a(k + PFA);
+      else load_t(k + PFA - KS);  // the first gradient steps' operands
+      const int sub = k / NS, st = k % NS;
+      sc[sub] = M::mma(fq[k], kf[st], sc[sub]);
+      dpv[sub] = M::mma(fo[k], vf[st], dpv[sub]);
+      if (sub == 1) {
+#pragma unroll
+        for (int i = 0; i < JS; ++i) prob(0, st * JS + i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      if (k + PFT < KG) load_t(k + PFT);
+      const int sub = k / (2 * ND), tt = (k / ND) % 2, dt = k % ND;
+      if (sub == 0) {
+#pragma unroll
+        for (int i = 0; i < JS; ++i) prob(1, k * JS + i);
+      }
+      dv[dt] = M::mma(to[k], pb[sub][tt], dv[dt]);
+      dk[dt] = M::mma(tq[k], db[sub][tt], dk[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   auto compute = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd) {
     const int32_t qt = cqt;
     advance(ch, cqt);
@@ -478,51 +618,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     if (causal && wk_lo > qp_hi) return;
     if (W > 0 && wk_hi <= qp_lo - W) return;
     const bool full = (!causal || wk_hi <= qp_lo) && (W <= 0 || wk_lo > qp_hi - W);
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = f32x16{};
-      dp[sub] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const int off = (sub * 32 + l32) * QT::PITCH + st * 16 + g * 8;
-        s[sub] = M::mma(*reinterpret_cast<const bf16x8 *>(sq + off), kf[st], s[sub]);
-        dp[sub] = M::mma(*reinterpret_cast<const bf16x8 *>(so + off), vf[st], dp[sub]);
-      }
-    }
-    float pv[2][16], ds[2][16];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int q4 = sub * 32 + 8 * a + 4 * g;  // rows c_row(4a..4a+3)
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sl + q4);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(sd + q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * a + e;
-          const float ex = fast_exp2(__builtin_fmaf(s[sub][j], p.scale_log2, -l4[e]));
-          pv[sub][j] = ex;
-          ds[sub][j] = ex * (dp[sub][j] - d4[e]);
-        }
-      }
-    if (!full) {  // wave-uniform
-      const int32_t qp_lane = qp_lo + 4 * g;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int32_t qp = qp_lane + (sub * 32 + 8 * (j >> 2) + (j & 3));
-          const bool vis = ((causal == 0) | (kp_lane <= qp)) & ((W <= 0) | (kp_lane > qp - W));
-          pv[sub][j] = vis ? pv[sub][j] : 0.f;
-          ds[sub][j] = vis ? ds[sub][j] : 0.f;
-        }
-    }
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      acc_transposed_all<ND>(dv, so, QT::PITCH, sub * 32, pv[sub], lane);
-      acc_transposed_all<ND>(dk, sq, QT::PITCH, sub * 32, ds[sub], lane);
-    }
+    // visible row offsets c (from the lane's first row qp_lo + 4g):
+    // causal: kp <= qp_lo + 4g + c; window: kp > qp_lo + 4g + c - W
+    const int32_t dk0 = kp_lane - (qp_lo + 4 * g);
+    const int32_t lo = (full || !causal) ? -(1 << 30) : dk0;
+    const int32_t hi = (full || W <= 0) ? (1 << 30) : dk0 + W;
+    body(sq, so, sl, sd, lo, (uint32_t)(hi - lo));
   };
 
   if (total > 0) stage(sQ0, sO0, sL0, sD0);
@@ -561,7 +662,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   constexpr int ND = D / 32;
   constexpr int KB = kFwdBN;
   static_assert(KB == 64, "tiles are 64 rows");
-  using KT = PadTile<D, D / 8 + 5>;  // row reads and transpose reads
+  // row reads and transpose reads: swizzled (D = 128) or padded (at most 2-way)
+  using KT = std::conditional_t<D == 128, SwzTile128, PadTile<D, D / 8 + 5>>;
   using VT = PadTile<D, D / 8 + 1>;  // row reads
   __shared__ __attribute__((aligned(1024))) bf16 sK0[KT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[VT::ELEMS];
@@ -622,6 +724,11 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   int koffs[KT::NJ], voffs[VT::NJ];
   tile_voffsets<KT>(koffs, kst, w, lane);
   tile_voffsets<VT>(voffs, vst, w, lane);
+  int ro[NS], trl[ND], trh[ND];  // swizzled K tile: per-lane read offsets
+  if constexpr (KT::kSwz) {
+    swz_row_offsets<NS>(ro, lane);
+    swz_tr_offsets<ND>(trl, trh, lane);
+  }
   // tile base pointers, advanced by one tile per stage
   const bf16 *kp = (const bf16 *)p.k + (int64_t)it.k0 * p.k_st + (int64_t)hk * p.k_sh;
   const bf16 *vp = (const bf16 *)p.v + (int64_t)it.k0 * p.v_st + (int64_t)hk * p.v_sh;
@@ -649,7 +756,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
       dp[sb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        s[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8), qf[st], s[sb]);
+        const int koff_ = KT::kSwz ? sb * 32 * 128 + ro[st] : (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8;
+        s[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sk + koff_), qf[st], s[sb]);
         dp[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8), of[st], dp[sb]);
       }
     }
@@ -685,7 +793,10 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
       }
     }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds[sb], lane);
+    for (int sb = 0; sb < 2; ++sb) {
+      if constexpr (KT::kSwz) acc_transposed_swz<ND>(dq, sk, sb * 32, trl, trh, ds[sb]);
+      else acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds[sb], lane);
+    }
   };
 
   if (it.k0 < k1) stage(sK0, sV0, it.k0);

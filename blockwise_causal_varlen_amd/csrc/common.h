@@ -140,7 +140,46 @@ template <int D, int PCH> struct PadTile {
   static constexpr int NJ = (NBLK + 3) / 4;    // blocks per wave (4 waves)
   static constexpr int PITCH = PCH * 8;        // elements per row
   static constexpr int ELEMS = 64 * PITCH;     // elements per tile
+  static constexpr bool kSwz = false;
 };
+
+// Swizzled tile of 64 rows x 128 bf16 (16 chunks a row, no padding): row r
+// keeps its logical chunk c in physical chunk c ^ swz128(r), with
+// swz128(r) = 4 (r mod 4) + (r / 4 mod 4). With 64 banks of 4 bytes a row is
+// one pass over all banks, and a physical chunk is 4 banks. A b128 read pass
+// (16 lanes: 16 consecutive rows, one chunk) then sees 16 distinct swizzles,
+// and a transpose read pass (32 lanes: 4 aligned rows x 4 aligned chunks)
+// puts each row in its own quarter of the chunks: both are conflict free,
+// where a padded pitch can serve only one of the two patterns.
+struct SwzTile128 {
+  static constexpr int CPR = 16, NBLK = 16, NJ = 4, PITCH = 128, ELEMS = 64 * PITCH;
+  static constexpr bool kSwz = true;
+};
+__device__ __forceinline__ int swz128(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// Per-lane element offsets into a SwzTile128. Row reads: row l32 (+ a
+// multiple of 16 rows, added by the caller), logical chunk 2 st + g.
+template <int NS>
+__device__ __forceinline__ void swz_row_offsets(int (&ro)[NS], int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) ro[st] = l32 * 128 + (((2 * st + g) ^ swz128(l32)) << 3);
+}
+// Transpose reads of d-tile dt: the lane's 16-lane group u = lane % 16 names
+// row 4 g + u / 4 (lo; + 8 for hi) of a 16-row block and columns
+// 32 dt + 16 dh + 4 (u % 4).. (dh = lane / 16 % 2).
+template <int ND>
+__device__ __forceinline__ void swz_tr_offsets(int (&lo)[ND], int (&hi)[ND], int lane) {
+  const int g = lane >> 5, u = lane & 15, dh = (lane >> 4) & 1;
+  const int sl = 4 * (u >> 2) + g, sh = sl ^ 2;  // swizzles of the lo and hi rows
+  const int rl = (4 * g + (u >> 2)) * 128;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    const int c = dt * 4 + dh * 2 + ((u & 3) >> 1);
+    lo[dt] = rl + ((c ^ sl) << 3) + 4 * (u & 1);
+    hi[dt] = rl + 8 * 128 + ((c ^ sh) << 3) + 4 * (u & 1);
+  }
+}
 
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kPastEnd = 0x40000000;   // a byte offset beyond any tile resource
@@ -159,7 +198,8 @@ __device__ __forceinline__ void tile_voffsets(int *voff, int64_t st, int wave, i
     const int blk = wave + 4 * j;
     const int s = blk * 64 + lane;
     const int r = s / TT::NBLK, c = s % TT::NBLK;
-    voff[j] = (blk < TT::NBLK && c < TT::CPR) ? (int)(r * st * 2) + c * 16 : kPastEnd;
+    const int cl = TT::kSwz ? (c ^ swz128(r)) : c;  // the logical chunk this slot holds
+    voff[j] = (blk < TT::NBLK && c < TT::CPR) ? (int)(r * st * 2) + cl * 16 : kPastEnd;
   }
 }
 
@@ -187,7 +227,8 @@ __device__ __forceinline__ void dma_tile_rows(bf16 *lds, RowPtr row_ptr, int wav
     if (blk < TT::NBLK) {
       const int s = blk * 64 + lane;
       const int r = s / TT::NBLK, c = s % TT::NBLK;
-      const bf16 *src = c < TT::CPR ? row_ptr(r) + c * 8 : row_ptr(0);
+      const int cl = TT::kSwz ? (c ^ swz128(r)) : c;
+      const bf16 *src = c < TT::CPR ? row_ptr(r) + cl * 8 : row_ptr(0);
       __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16, 0, 0);
     }
   }
