@@ -178,6 +178,9 @@ struct Problem {
   bool decode;
   bool paged;
   int32_t dsplit = 1, dsplit_len = 0;  // decode: split KV over dsplit waves per (sequence, kv head)
+  int32_t nsplit = 0;                   // tiled forward: > 1 = each query tile's keys cut in nsplit parts
+  bool gather = false;                  // paged keys copied to contiguous buffers first
+  int64_t gather_row_bytes = 0;         // bytes of one gathered logical row (all heads) of K or V
 };
 
 attn_status check_qkv(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v) {
@@ -196,7 +199,7 @@ attn_status check_qkv(const attn_tensor *q, const attn_tensor *k, const attn_ten
 }
 
 attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t num_seqs,
-                     int32_t max_q, int32_t max_k, const attn_mask *m, Problem &P) {
+                     int32_t max_q, int32_t max_k, const attn_mask *m, Problem &P, bool allow_split = true) {
   TRY(check_qkv(q, k, v));
   TRY(check_mask(m));
   if (num_seqs < 0 || max_q < 0 || max_k < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
@@ -227,6 +230,31 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
       P.dsplit_len = (int32_t)len;
     }
   }
+  // paged keys: a streaming gather of the logical rows into contiguous
+  // workspace buffers, then the contiguous forward (page lookups inside the
+  // forward's tile loop measured 1.5x slower than gather + contiguous)
+  P.gather = P.paged;
+  if (P.paged) {
+    P.gather_row_bytes = k->n_head * k->head_dim * (int64_t)esize(k->dtype);
+    if ((m->page_stride * esize(k->dtype)) % 16)
+      return fail(ATTN_ERR_LAYOUT, "page_stride must be a multiple of 16 bytes");
+  }
+  P.nsplit = 0;
+  if (allow_split && !P.decode && P.nseg == 0 && max_k >= 1024) {
+    // few query-tile workgroups (the chip holds 512): cut each tile's visible
+    // keys into parts (>= 512 keys of max_k each, at most 16), computed as
+    // segments and merged the same way
+    const int64_t wgs = ((int64_t)P.n_q / kFwdBM + num_seqs) * P.hq;
+    if (wgs > 0 && wgs < 512) {
+      int64_t n = (1024 + wgs - 1) / wgs;
+      if (n > 16) n = 16;
+      if (n > max_k / 512) n = max_k / 512;
+      if (n > 1) {
+        P.nsplit = (int32_t)n;
+        P.nseg = n;
+      }
+    }
+  }
   return check_ranges(q, k, v, m, P.n_k_logical);
 }
 
@@ -242,6 +270,7 @@ size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs) {
     b += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
     b += align256((size_t)P.nseg * P.hq * P.n_q * 4);
   }
+  if (P.gather) b += 2 * align256((size_t)P.n_k_logical * P.gather_row_bytes);  // gathered K, V (last)
   return b;
 }
 
@@ -329,9 +358,10 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
                            int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
                            const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
-                           void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr) {
+                           void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr,
+                           bool allow_split = true) {
   Problem P;
-  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm));
   TRY(check_out(out, P, "out"));
   if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
@@ -368,6 +398,31 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
                      "split-KV merge");
   }
 
+  attn_tensor kg, vg;
+  attn_mask mg;
+  if (P.gather) {
+    // logical rows of the paged caches -> contiguous K, V at the workspace's end
+    const size_t gb = align256((size_t)P.n_k_logical * P.gather_row_bytes);
+    char *gk = (char *)workspace + need - 2 * gb;
+    PageGatherArgs ga;
+    ga.src_k = k->data; ga.src_v = v->data;
+    ga.page_stride = mask->page_stride; ga.st = k->stride_tok; ga.sh = k->stride_head;
+    if (v->stride_tok != k->stride_tok || v->stride_head != k->stride_head)
+      return fail(ATTN_ERR_LAYOUT, "paged k and v caches must share their strides");
+    ga.table = mask->block_table; ga.max_blocks = mask->max_blocks; ga.n_pages = k->n_tok / mask->block_size;
+    ga.shift = __builtin_ctz((unsigned)mask->block_size);
+    ga.dst_k = gk; ga.dst_v = gk + gb;
+    ga.n_rows = P.n_k_logical; ga.h = (int32_t)P.hkv; ga.d = (int32_t)P.d; ga.eb = esize(k->dtype);
+    TRY(hip_check(timed("attn_gather", s, [&] { return launch_page_gather(ga, s); }), "page gather"));
+    kg = *k;
+    kg.data = gk; kg.n_tok = P.n_k_logical; kg.stride_head = P.d; kg.stride_tok = P.hkv * P.d;
+    vg = kg;
+    vg.data = gk + gb;
+    mg = *mask;
+    mg.block_table = nullptr; mg.max_blocks = 0; mg.page_stride = 0;
+    k = &kg; v = &vg; mask = &mg;
+    P.paged = false;
+  }
   const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
   char *w = (char *)workspace;
   SchedBufs sb = sched_carve(w, cap);
@@ -379,18 +434,13 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
   } else {
     TRY(hip_check(timed("attn_sched", s, [&] {
                     return launch_schedule(cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, P.n_k_logical, md, kFwdBM,
-                                           kFwdBN, 0, (int32_t)P.nseg, sb, s);
+                                           kFwdBN, 0, (int32_t)P.nseg, sb, s, P.nsplit);
                   }), "scheduler"));
   }
   FwdArgs a;
   a.q = tdev(q); a.k = tdev(k); a.v = tdev(v);
   a.dtype = q->dtype; a.head_dim = (int32_t)P.d; a.hq = (int32_t)P.hq; a.hkv = (int32_t)P.hkv;
   a.scale = scale; a.mask = md;
-  a.block_table = P.paged ? mask->block_table : nullptr;
-  a.block_size = mask ? mask->block_size : 0;
-  a.max_blocks = mask ? mask->max_blocks : 0;
-  a.page_stride = mask ? mask->page_stride : 0;
-  a.n_pages = P.paged ? k->n_tok / mask->block_size : 0;
   a.out = out->data; a.out_dtype = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
   a.lse = lse; a.lse_n = P.n_q;
   a.part_out = nullptr; a.part_lse = nullptr;
@@ -421,6 +471,8 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     mn.plse[0] = a.part_lse;
     mn.out = out->data; mn.out_dtype = out->dtype; mn.o_st = out->stride_tok; mn.o_sh = out->stride_head;
     mn.lse = lse; mn.n = P.n_q; mn.h = P.hq; mn.d = P.d;
+    // rows no tile reaches (outside the query view or of no document) stay untouched
+    mn.cu = cu_seqlens_q; mn.num_seqs = num_seqs; mn.view = mask ? (int32_t)mask->q_view : 0;
     TRY(hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(mn, s); }), "segment merge"));
   }
   return ok();
@@ -928,18 +980,18 @@ attn_status run_ring_fwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
     if (fuse) {
       const FusedMerge fm{out_acc, s > 0, (s == last_front ? 1 : 0) | (s == last_back ? 2 : 0)};
       TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, out, lse,
-                         fws, fws_bytes, stream, &fm, pre));
+                         fws, fws_bytes, stream, &fm, pre, false));
       continue;
     }
     if (s == 0) {
       // the first block initialises the running state
       const attn_tensor *dst = (n_steps == 1) ? out : out_acc;
       TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, dst, lse,
-                         fws, fws_bytes, stream, nullptr, pre));
+                         fws, fws_bytes, stream, nullptr, pre, false));
       continue;
     }
     TRY(block_fwd_impl(q, &k_loc[src], &v_loc[src], cu, cu, num_seqs, max_local, max_local, &m, scale, &bout, blse,
-                       fws, fws_bytes, stream, nullptr, pre));
+                       fws, fws_bytes, stream, nullptr, pre, false));
     TRY(attn_merge_out_lse(out_acc, lse, &bout, blse, cu, num_seqs, m.q_view, nullptr, last ? out : nullptr, 0,
                            stream));
   }

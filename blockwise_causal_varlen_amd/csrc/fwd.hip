@@ -5,9 +5,10 @@
 // zigzag_ring_attention, `_block_forward`; ring_attention, `_fa_forward`):
 // returns the block's normalised output and its log-sum-exp of scaled scores.
 // Masks: causal and sliding window on explicit positions, per-document
-// front/back half views, a round-robin key position map and paged keys (AWS
-// NKI "Attention KV-Parallel Segmented CTE": block_tables, kvp_group_size,
-// sliding_window, seg_size).
+// front/back half views and a round-robin key position map (AWS NKI
+// "Attention KV-Parallel Segmented CTE": kvp_group_size, sliding_window,
+// seg_size). Paged keys (its block_tables) are gathered into contiguous rows
+// before the forward runs.
 //
 // Kernel shape. A workgroup = 4 waves = 128 query rows of one q head; wave w
 // owns rows [32w, 32w+32). Scores are computed transposed, S^T = K Q^T, with
@@ -128,6 +129,14 @@ __device__ void make_item(const SchedParams &p, int64_t qs, int64_t qe, int64_t 
     const int64_t sa = ks + sg * m.seg_size, sbd = sa + m.seg_size;
     if (sa > lo) lo = sa;
     if (sbd < hi) hi = sbd;
+  } else if (p.nsplit > 1 && hi > lo) {
+    // part sg of the visible keys, in whole key tiles
+    int64_t chunk = (hi - lo + p.nsplit - 1) / p.nsplit;
+    chunk = (chunk + p.key_tile - 1) / p.key_tile * p.key_tile;
+    const int64_t a = lo + sg * chunk;
+    const int64_t b = a + chunk < hi ? a + chunk : hi;
+    lo = a < hi ? a : hi;
+    hi = b;
   }
   if (hi < lo) hi = lo;
   it.q0 = (int32_t)q0; it.q1 = (int32_t)q1;
@@ -154,6 +163,7 @@ __device__ void sched_run(const SchedParams &p) {
       view_range(ks, ke, m.k_view, ka, kb);
       ntile = p.by_keys ? (kb - ka + p.tile - 1) / p.tile : (qb - qa + p.tile - 1) / p.tile;
       if (m.seg_size > 0 && !p.by_keys) nseg = (ke - ks + m.seg_size - 1) / m.seg_size;
+      else if (p.nsplit > 1 && !p.by_keys) nseg = p.nsplit;
       if (nseg > p.max_seg) nseg = p.max_seg;
       if (nseg < 1) nseg = 1;
     }
@@ -223,8 +233,8 @@ __global__ __launch_bounds__(kSchedThreads) void sched_batch_kernel(SchedBatch b
 
 hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs, int64_t n_q,
                            int64_t n_k, const MaskDev &m, int32_t tile, int32_t key_tile,
-                           int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s) {
-  SchedParams p{cu_q, cu_k, num_seqs, n_q, n_k, m, tile, key_tile, by_keys, max_seg < 1 ? 1 : max_seg, sb};
+                           int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s, int32_t nsplit) {
+  SchedParams p{cu_q, cu_k, num_seqs, n_q, n_k, m, tile, key_tile, by_keys, max_seg < 1 ? 1 : max_seg, sb, nsplit};
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, s, p);
   return hipGetLastError();
 }
@@ -249,9 +259,6 @@ struct FwdParams {
   int32_t hq, group;
   float scale_log2;
   MaskDev m;
-  const int32_t *block_table;
-  int32_t block_size, max_blocks;
-  int64_t page_stride, n_pages;
   void *out; int64_t o_st, o_sh;
   float *lse; int64_t lse_n;
   int32_t segmented;
@@ -272,19 +279,6 @@ template <> struct Tile<float> {
   template <int D> static constexpr int kpitch() { return D + 1; }
   template <int D> static constexpr int vpitch() { return D + 4; }
 };
-
-// Address of logical key row j (head hk) of a K or V tensor; nullptr when the
-// row has no valid page.
-template <typename T>
-__device__ __forceinline__ const T *key_row(const FwdParams &p, const T *base, int64_t st, int64_t sh,
-                                            int64_t j, int hk) {
-  if (p.block_table == nullptr) return base + j * st + hk * sh;
-  const int64_t b = j / p.block_size;
-  if (b >= p.max_blocks) return nullptr;
-  const int64_t pg = p.block_table[b];
-  if (pg < 0 || pg >= p.n_pages) return nullptr;
-  return base + pg * p.page_stride + hk * sh + (j - b * p.block_size) * st;
-}
 
 template <typename T, int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
@@ -354,10 +348,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       const int64_t j = kt + kr;
       i32x4 kv4 = {0, 0, 0, 0}, vv4 = {0, 0, 0, 0};
       if (j < it.k1) {
-        const T *ka = key_row<T>(p, kb, p.k_st, p.k_sh, j, hk);
-        const T *va = key_row<T>(p, vb, p.v_st, p.v_sh, j, hk);
-        if (ka) kv4 = ld16(ka + col);
-        if (va) vv4 = ld16(va + col);
+        kv4 = ld16(kb + j * p.k_st + (int64_t)hk * p.k_sh + col);
+        vv4 = ld16(vb + j * p.v_st + (int64_t)hk * p.v_sh + col);
       }
       if constexpr (kBf16) {
         st16(&sK[kr * KP + col], kv4);
@@ -509,59 +501,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   if (g == 0) p.lse[(int64_t)h * p.lse_n + row] = lse_v;
 }
 
-// Paged K/V tiles (block size 2^shift). Each lane's DMA block j of a tile
-// reads one row; paged_pages loads the physical page of that row for tile kt
-// (issued one tile ahead of the copy, so the table read is off the critical
-// path), dma_paged then copies the tile with those pages.
-template <typename TT>
-__device__ __forceinline__ int paged_row(int blk, int lane, int &col) {
-  const int s = blk * 64 + lane;
-  const int r = s / TT::NBLK, c = s - r * TT::NBLK;
-  col = c < TT::CPR ? c * 8 : 0;  // padding chunks re-read column 0 of their row
-  return c < TT::CPR ? r : 0;
-}
-template <typename TT>
-__device__ __forceinline__ void paged_pages(int (&pg)[TT::NJ], const int32_t *table, int32_t max_blocks, int shift,
-                                            int32_t kt, int32_t k1, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < TT::NJ; ++j) {
-    const int blk = wave + 4 * j;
-    if (blk < TT::NBLK) {
-      int col;
-      const int32_t r = paged_row<TT>(blk, lane, col);
-      const int32_t t = kt + r < k1 ? kt + r : k1 - 1;
-      const int32_t b = t >> shift;
-      pg[j] = table[b < max_blocks ? b : 0];
-    }
-  }
-}
-template <typename TT>
-__device__ __forceinline__ void dma_paged(bf16 *lds, const bf16 *base, int64_t page_stride, int64_t head_off,
-                                          int64_t st, const int (&pg)[TT::NJ], int32_t max_blocks, int64_t n_pages,
-                                          int shift, int32_t kt, int32_t k1, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < TT::NJ; ++j) {
-    const int blk = wave + 4 * j;
-    if (blk < TT::NBLK) {
-      int col;
-      const int32_t r = paged_row<TT>(blk, lane, col);
-      const int32_t t = kt + r < k1 ? kt + r : k1 - 1;  // rows past the end: a valid row, masked later
-      const int32_t b = t >> shift;
-      const int64_t page = pg[j];
-      const bool ok = b < max_blocks && page >= 0 && page < n_pages;
-      const bf16 *src = ok ? base + page * page_stride + head_off + (int64_t)(t & ((1 << shift) - 1)) * st + col : base;
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16, 0, 0);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // bf16 forward: K/V tiles arrive by asynchronous global->LDS copies into two
 // swizzled buffers, so tile t+1 is in flight while tile t is computed; one
 // barrier per tile. The loop is unrolled by two so that every LDS read names
 // a fixed buffer (the compiler then only waits for the copy at the barrier).
 // ---------------------------------------------------------------------------
-template <int D, typename OutT, bool PAGED>
+template <int D, typename OutT>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
@@ -633,37 +579,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const bf16 *vb = (const bf16 *)p.v;
   const int32_t kst = (int32_t)p.k_st, vst = (int32_t)p.v_st;
   int koffs[KT::NJ], voffs[VT::NJ];
-  if constexpr (!PAGED) {
-    tile_voffsets<KT>(koffs, kst, w, lane);
-    tile_voffsets<VT>(voffs, vst, w, lane);
-  }
+  tile_voffsets<KT>(koffs, kst, w, lane);
+  tile_voffsets<VT>(voffs, vst, w, lane);
   // tile base pointers, advanced by one tile per stage
   const bf16 *kp = kb + (int64_t)it.k0 * p.k_st + (int64_t)hk * p.k_sh;
   const bf16 *vp = vb + (int64_t)it.k0 * p.v_st + (int64_t)hk * p.v_sh;
-  int kpg[KT::NJ], vpg[VT::NJ];  // paged keys: pages of the next tile to stage
-  if constexpr (PAGED) {
-    if (it.k0 < k1) {
-      paged_pages<KT>(kpg, p.block_table, p.max_blocks, SH, it.k0, k1, w, lane);
-      paged_pages<VT>(vpg, p.block_table, p.max_blocks, SH, it.k0, k1, w, lane);
-    }
-  }
   auto stage = [&](bf16 *sk, bf16 *sv, int32_t kt) {
-    if constexpr (!PAGED) {
-      const int32_t nvalid = k1 - kt < BN ? k1 - kt : BN;
-      dma_tile_buf<KT>(sk, kp, ((nvalid - 1) * kst + D) * 2, koffs, w);
-      dma_tile_buf<VT>(sv, vp, ((nvalid - 1) * vst + D) * 2, voffs, w);
-      kp += BN * (int64_t)kst;
-      vp += BN * (int64_t)vst;
-    } else {
-      dma_paged<KT>(sk, kb, p.page_stride, (int64_t)hk * p.k_sh, p.k_st, kpg, p.max_blocks, p.n_pages, SH, kt, k1, w,
-                    lane);
-      dma_paged<VT>(sv, vb, p.page_stride, (int64_t)hk * p.v_sh, p.v_st, vpg, p.max_blocks, p.n_pages, SH, kt, k1, w,
-                    lane);
-      if (kt + BN < k1) {  // the next tile's pages
-        paged_pages<KT>(kpg, p.block_table, p.max_blocks, SH, kt + BN, k1, w, lane);
-        paged_pages<VT>(vpg, p.block_table, p.max_blocks, SH, kt + BN, k1, w, lane);
-      }
-    }
+    const int32_t nvalid = k1 - kt < BN ? k1 - kt : BN;
+    dma_tile_buf<KT>(sk, kp, ((nvalid - 1) * kst + D) * 2, koffs, w);
+    dma_tile_buf<VT>(sv, vp, ((nvalid - 1) * vst + D) * 2, voffs, w);
+    kp += BN * (int64_t)kst;
+    vp += BN * (int64_t)vst;
   };
 
   auto compute = [&](const bf16 *sk, const bf16 *sv, int32_t kt) {
@@ -840,14 +766,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    const bool paged = fp.block_table != nullptr;
-    if (out_dtype == 0) {
-      if (paged) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-    } else {
-      if (paged) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-    }
+    if (out_dtype == 0) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, float>), dim3((unsigned)grid), dim3(256), 0, s, fp);
   } else {
     if (out_dtype == 0)
       hipLaunchKernelGGL((fwd_kernel<T, D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
@@ -864,8 +784,6 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   fp.hq = a.hq; fp.group = a.hq / a.hkv;
   fp.scale_log2 = a.scale * kLog2e;
   fp.m = a.mask;
-  fp.block_table = a.block_table; fp.block_size = a.block_size; fp.max_blocks = a.max_blocks;
-  fp.page_stride = a.page_stride; fp.n_pages = a.n_pages;
   fp.out = a.out; fp.o_st = a.o_st; fp.o_sh = a.o_sh;
   fp.lse = a.lse; fp.lse_n = a.lse_n;
   fp.segmented = a.part_out != nullptr;

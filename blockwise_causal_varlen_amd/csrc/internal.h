@@ -64,6 +64,7 @@ struct SchedJob {
   int32_t by_keys;  // 0: tiles of query rows; 1: tiles of key rows (dK/dV)
   int32_t max_seg;  // segments the partial buffers hold (longer documents are cut)
   SchedBufs sb;
+  int32_t nsplit = 0;  // > 1 (query tiles, no segments): cut each tile's visible keys in nsplit parts
 };
 constexpr int kMaxSchedJobs = 8;
 // n (<= kMaxSchedJobs) independent schedules in one launch
@@ -71,7 +72,8 @@ hipError_t launch_schedules(const SchedJob *jobs, int n, hipStream_t s);
 
 hipError_t launch_schedule(const int32_t *cu_q, const int32_t *cu_k, int32_t num_seqs,
                            int64_t n_q, int64_t n_k, const MaskDev &m, int32_t tile,
-                           int32_t key_tile, int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s);
+                           int32_t key_tile, int32_t by_keys, int32_t max_seg, SchedBufs sb, hipStream_t s,
+                           int32_t nsplit = 0);
 
 struct FwdArgs {
   TensorDev q, k, v;
@@ -80,9 +82,6 @@ struct FwdArgs {
   int32_t hq, hkv;
   float scale;
   MaskDev mask;
-  const int32_t *block_table;  // NULL = not paged
-  int32_t block_size, max_blocks;
-  int64_t page_stride, n_pages;
   // outputs: either final (out/lse) or segment partials (part_*)
   void *out; int32_t out_dtype; int64_t o_st, o_sh;
   float *lse; int64_t lse_n;    // lse[h * lse_n + row]
@@ -136,8 +135,24 @@ struct MergeNArgs {
   void *out; int32_t out_dtype; int64_t o_st, o_sh;
   float *lse;
   int64_t n, h, d;
+  // non-null cu: only rows of the documents (in `view` of each) are written
+  const int32_t *cu = nullptr; int32_t num_seqs = 0, view = 0;
 };
 hipError_t launch_merge_n(const MergeNArgs &a, hipStream_t s);
+
+// Copy of the logical rows [0, n_rows) of paged K and V caches into
+// contiguous [n_rows, h, d] buffers (strides in elements, eb bytes an element).
+struct PageGatherArgs {
+  const void *src_k, *src_v;
+  int64_t page_stride, st, sh;
+  const int32_t *table;
+  int64_t max_blocks, n_pages;
+  int32_t shift;
+  void *dst_k, *dst_v;
+  int64_t n_rows;
+  int32_t h, d, eb;
+};
+hipError_t launch_page_gather(const PageGatherArgs &a, hipStream_t s);
 
 struct DeltaArgs {
   const void *dout; int32_t dtype_do; int64_t do_st, do_sh;

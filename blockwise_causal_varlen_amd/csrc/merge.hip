@@ -393,47 +393,53 @@ hipError_t launch_out_transpose(const TransposeArgs &a, hipStream_t s) {
 // the partials of the ranks are combined by online softmax):
 //   lse = m + log(sum_i exp(lse_i - m)),  out = sum_i exp(lse_i - lse) out_i
 // ---------------------------------------------------------------------------
+// One workgroup streams one row (all heads) at a time; with a.cu set, rows of
+// no document, or outside the view, are left as they are.
 template <int D, typename OT>
 __global__ __launch_bounds__(256) void merge_n_kernel(MergeNArgs a) {
-  constexpr int G = D / 4;
-  const int64_t total = a.n * a.h;
-  const int sub = threadIdx.x % G;
-  const int64_t per_blk = 256 / G;
-  for (int64_t pr = blockIdx.x * per_blk + threadIdx.x / G; pr < total; pr += (int64_t)gridDim.x * per_blk) {
-    const int64_t row = pr / a.h;
-    const int64_t h = pr - row * a.h;
-    const int64_t li = h * a.n + row;
-    // part i: explicit pointers, or (strided) part 0 advanced by i strides
-    auto plse = [&](int i) -> float {
-      return a.strided ? a.plse[0][li + i * a.lse_stride] : a.plse[i][li];
-    };
-    float mx = neg_inf();
-    for (int i = 0; i < a.n_parts; ++i) mx = fmaxf(mx, plse(i));
-    f32x4 acc = f32x4{};
-    float ln = neg_inf();
-    if (mx != neg_inf()) {
-      float z = 0.f;
-      for (int i = 0; i < a.n_parts; ++i) z += expf(plse(i) - mx);
-      ln = mx + logf(z);
-      for (int i = 0; i < a.n_parts; ++i) {
-        const float wgt = expf(plse(i) - ln);
-        if (wgt == 0.f) continue;
-        const int pi = a.strided ? 0 : i;
-        const int64_t off = a.strided ? i * a.out_stride : 0;
-        f32x4 v = a.pdtype[pi] == 0
-                      ? ld4<bf16>((const bf16 *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub)
-                      : ld4<float>((const float *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub);
-        acc += wgt * v;
-      }
+  constexpr int G = D / 4;     // lanes per (row, head)
+  constexpr int HP = 256 / G;  // heads per pass
+  const int sub = threadIdx.x % G, hl = threadIdx.x / G;
+  const int H = (int)a.h;
+  for (int64_t row = blockIdx.x; row < a.n; row += gridDim.x) {
+    if (a.cu) {
+      if (a.num_seqs <= 0 || row < a.cu[0] || row >= a.cu[a.num_seqs]) continue;
+      if (!row_in_view(a.cu, a.num_seqs, a.view, row)) continue;
     }
-    st4<OT>((OT *)a.out + row * a.o_st + h * a.o_sh + 4 * sub, acc);
-    if (sub == 0) a.lse[li] = ln;
+    for (int h = hl; h < H; h += HP) {
+      const int64_t li = (int64_t)h * a.n + row;
+      // part i: explicit pointers, or (strided) part 0 advanced by i strides
+      auto plse = [&](int i) -> float {
+        return a.strided ? a.plse[0][li + i * a.lse_stride] : a.plse[i][li];
+      };
+      float mx = neg_inf();
+      for (int i = 0; i < a.n_parts; ++i) mx = fmaxf(mx, plse(i));
+      f32x4 acc = f32x4{};
+      float ln = neg_inf();
+      if (mx != neg_inf()) {
+        float z = 0.f;
+        for (int i = 0; i < a.n_parts; ++i) z += expf(plse(i) - mx);
+        ln = mx + logf(z);
+        for (int i = 0; i < a.n_parts; ++i) {
+          const float wgt = expf(plse(i) - ln);
+          if (wgt == 0.f) continue;
+          const int pi = a.strided ? 0 : i;
+          const int64_t off = a.strided ? i * a.out_stride : 0;
+          f32x4 v = a.pdtype[pi] == 0
+                        ? ld4<bf16>((const bf16 *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub)
+                        : ld4<float>((const float *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub);
+          acc += wgt * v;
+        }
+      }
+      st4<OT>((OT *)a.out + row * a.o_st + h * a.o_sh + 4 * sub, acc);
+      if (sub == 0) a.lse[li] = ln;
+    }
   }
 }
 
 hipError_t launch_merge_n(const MergeNArgs &a, hipStream_t s) {
   if (a.n * a.h == 0) return hipSuccess;
-  const unsigned grid = stream_grid(a.n * a.h, 256 / (a.d / 4));
+  const unsigned grid = row_grid(a.n);
   if (a.d == 128) {
     if (a.out_dtype == 0) hipLaunchKernelGGL((merge_n_kernel<128, bf16>), dim3(grid), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((merge_n_kernel<128, float>), dim3(grid), dim3(256), 0, s, a);
@@ -573,6 +579,44 @@ hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int6
   const unsigned gx = (unsigned)((max_local + 3) / 4);
   if (gx == 0) return hipSuccess;
   hipLaunchKernelGGL(zigzag_shard_kernel, dim3(gx, (unsigned)num_seqs), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Paged-cache gather (NKI KV-parallel prefill's block_table, Parameters): the
+// logical key row t of a paged cache sits at page table[t >> shift], row
+// t & (2^shift - 1) of it. One wave copies one logical row (all heads, K and V)
+// into contiguous [rows, H, D] buffers; rows of an invalid page read as zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void page_gather_kernel(PageGatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t per_head = (int64_t)a.d * a.eb;
+  const int64_t row_bytes = per_head * a.h;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < a.n_rows; t += (int64_t)gridDim.x * 4) {
+    const int64_t b = t >> a.shift;
+    const int64_t pg = b < a.max_blocks ? a.table[b] : -1;
+    const bool ok = pg >= 0 && pg < a.n_pages;
+    const int64_t prow = t & ((1 << a.shift) - 1);
+    for (int64_t off = lane * 16; off < row_bytes; off += 64 * 16) {
+      const int64_t hh = off / per_head, dd = off - hh * per_head;
+      const int64_t so = (pg * a.page_stride + hh * a.sh + prow * a.st) * a.eb + dd;
+      const int64_t dof = t * row_bytes + off;
+      i32x4 vk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (ok) {
+        vk = ld16((const char *)a.src_k + so);
+        vv = ld16((const char *)a.src_v + so);
+      }
+      st16((char *)a.dst_k + dof, vk);
+      st16((char *)a.dst_v + dof, vv);
+    }
+  }
+}
+
+hipError_t launch_page_gather(const PageGatherArgs &a, hipStream_t s) {
+  if (a.n_rows <= 0) return hipSuccess;
+  int64_t b = (a.n_rows + 3) / 4;
+  if (b > 256 * 16) b = 256 * 16;
+  hipLaunchKernelGGL(page_gather_kernel, dim3((unsigned)b), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

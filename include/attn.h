@@ -137,7 +137,8 @@ typedef struct {
                              two when kv_interleave > 0 or block_table is set) */
   int32_t max_blocks;     /* entries in block_table */
   const int32_t *block_table; /* device; NULL = not paged */
-  int64_t page_stride;    /* elements between pages (paged only) */
+  int64_t page_stride;    /* elements between pages (paged only; a multiple
+                             of 16 bytes, else ATTN_ERR_LAYOUT) */
   int32_t seg_size;       /* 0 = no split */
   int32_t reserved;
 } attn_mask;
@@ -170,7 +171,14 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
  *   scale: multiplies q.k before the softmax (callers pass 1/sqrt(D) for the
  *          pages' default, [ULY] `cached_ulysses_attention` scale)
  * D must be 64 or 128. mask == NULL means full (no causal, all rows).
- * Workspace: attn_workspace_size(ATTN_OP_BLOCK_FWD, ...) bytes.
+ * Workspace: attn_workspace_size(ATTN_OP_BLOCK_FWD, ...) bytes. It holds,
+ * besides the tile schedule: the max_blocks * block_size logical rows of paged
+ * K and V (gathered into contiguous rows before the forward; rows of pages
+ * outside [0, n_tok / block_size) read as zero); the per-segment partials when
+ * seg_size > 0; and, when few 128-row query tiles face many keys (fewer than
+ * 512 tile x head workgroups and max_seqlen_k >= 1024, no segments), the
+ * partials of each tile's visible keys cut into up to 16 parts, merged like
+ * segments. Rows outside the q view stay untouched in every case.
  */
 attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,

@@ -102,6 +102,47 @@ def test_block_fwd_untouched_rows_stay(gpu_lib):
     assert torch.all(o[32:64] != 7.0)
 
 
+SPLIT_MASKS = {
+    "causal_end": dict(causal=True, q_pos_offset=2900),   # query rows at the end of the keys
+    "window": dict(causal=True, q_pos_offset=4000, window=700),
+    "full": dict(),
+    "q_back": dict(q_view="back"),
+    "roundrobin": dict(causal=True, q_pos_offset=9000, kv_interleave=4, kv_rank=3, block_size=16),
+}
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("mname", list(SPLIT_MASKS))
+def test_block_fwd_split_keys(gpu_lib, dtype, d, mname):
+    """Few query tiles against thousands of keys: the forward cuts each query
+    tile's visible keys into parts (workspace grows by the partials) and
+    merges them; every element against the oracle, untouched rows kept."""
+    L = gpu_lib
+    lens, klens = [96, 200], [3000, 5000]
+    hq, hkv = 4, 1
+    cu_q, cu_k, q, k, v = rand_case(lens, hq, hkv, d, dtype, seed=41, k_lens=klens)
+    mk = SPLIT_MASKS[mname]
+    scale = 1.0 / math.sqrt(d)
+    say(f"block_fwd split {mname} {dtype} D={d}")
+    ws = L.attn_workspace_size(L.OP_BLOCK_FWD, L.desc(q), L.desc(k), len(lens), max(lens), max(klens), L.mask(**mk))
+    assert ws >= 2 * q.shape[0] * hq * d * 4, ws   # at least two key parts
+    ref_o, ref_l = O.block_forward(q, k, v, cu_q, cu_k, scale, **mk)
+    out = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda")
+    lse = torch.full((hq, q.shape[0]), 9.0, dtype=torch.float32, device="cuda")
+    L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu_q, cu_k, max(lens), max(klens), scale, L.mask(**mk),
+                out=out, lse=lse)
+    torch.cuda.synchronize()
+    o, l = out.cpu(), lse.cpu()
+    rows = np.arange(q.shape[0])
+    if mname == "q_back":
+        front = np.r_[0:48, 96:196]
+        assert torch.all(o[front] == 7.0) and torch.all(l[:, front] == 9.0)
+        rows = np.r_[48:96, 196:296]
+    tol = OUT_TOL if dtype == torch.bfloat16 else 1e-4
+    assert_close_rows(o, l, ref_o, ref_l, rows=rows, out_tol=tol,
+                      lse_tol=LSE_TOL if dtype == torch.bfloat16 else 1e-4, what=mname)
+
+
 @pytest.mark.parametrize("bdtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("view", ["all", "back", "front"])
 def test_merge_matches_oracle(gpu_lib, bdtype, view):
