@@ -217,23 +217,6 @@ __device__ __forceinline__ void dma_tile_buf(bf16 *lds, const bf16 *tile_row0, i
   }
 }
 
-// Asynchronous tile copy from per-row global addresses (paged keys).
-// row_ptr(r) must return a valid address for every r in [0, 64).
-template <class TT, typename RowPtr>
-__device__ __forceinline__ void dma_tile_rows(bf16 *lds, RowPtr row_ptr, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < TT::NJ; ++j) {
-    const int blk = wave + 4 * j;
-    if (blk < TT::NBLK) {
-      const int s = blk * 64 + lane;
-      const int r = s / TT::NBLK, c = s % TT::NBLK;
-      const int cl = TT::kSwz ? (c ^ swz128(r)) : c;
-      const bf16 *src = c < TT::CPR ? row_ptr(r) + cl * 8 : row_ptr(0);
-      __builtin_amdgcn_global_load_lds(src, (lds_void *)(reinterpret_cast<char *>(lds) + blk * 1024), 16, 0, 0);
-    }
-  }
-}
-
 // Transpose read of a padded tile (pitch in elements): the lane's 16-lane
 // group u = lane % 16 supplies row r0 + u/4, columns col0 + 4*(u%4)..+3, and
 // receives rows r0..r0+3 of column col0 + u.
