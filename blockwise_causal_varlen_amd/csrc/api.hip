@@ -363,7 +363,7 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
   Problem P;
   TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm));
   TRY(check_out(out, P, "out"));
-  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!lse && P.n_q > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
   const size_t need = fwd_ws_bytes(P, num_seqs);
@@ -506,7 +506,7 @@ attn_status attn_merge_out_lse(const attn_tensor *out, float *lse, const attn_te
     if (final_out->n_tok != out->n_tok || final_out->n_head != out->n_head || final_out->head_dim != out->head_dim)
       return fail(ATTN_ERR_SHAPE, "final_out shape differs from out");
   }
-  if (!lse || !block_lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if ((!lse || !block_lse) && out->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (q_view > 2) return fail(ATTN_ERR_INVALID, "bad view %u", q_view);
   if (q_view != 0 && (!cu_seqlens || num_seqs <= 0)) return fail(ATTN_ERR_NULL, "a view needs cu_seqlens");
   MergeArgs a;
@@ -572,7 +572,7 @@ attn_status attn_merge_diag(const attn_tensor *q, const attn_tensor *k, const at
     if (final_out->n_tok != q->n_tok || final_out->n_head != q->n_head || final_out->head_dim != q->head_dim)
       return fail(ATTN_ERR_SHAPE, "final_out must be shaped like q");
   }
-  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
   a.out = (float *)out->data; a.o_st = out->stride_tok; a.o_sh = out->stride_head; a.lse = lse;
   a.fout = final_out ? final_out->data : nullptr;
@@ -592,7 +592,7 @@ attn_status attn_diag_bwd(const attn_tensor *dout, const attn_tensor *q, const a
   if (dout->dtype != q->dtype) return fail(ATTN_ERR_DTYPE, "dout dtype differs from q");
   if (dout->n_tok != q->n_tok || dout->n_head != q->n_head || dout->head_dim != q->head_dim)
     return fail(ATTN_ERR_SHAPE, "dout must be shaped like q");
-  if (!lse || !delta) return fail(ATTN_ERR_NULL, "lse / delta is NULL");
+  if ((!lse || !delta) && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse / delta is NULL");
   const attn_tensor *gr[3] = {dq, dk, dv};
   const char *gn[3] = {"dq", "dk", "dv"};
   for (int i = 0; i < 3; ++i) {
@@ -686,7 +686,7 @@ attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, floa
   TRY(check_hd(out->head_dim));
   if (dout->n_tok != out->n_tok || dout->n_head != out->n_head || dout->head_dim != out->head_dim)
     return fail(ATTN_ERR_SHAPE, "dout/out shapes differ");
-  if (!delta) return fail(ATTN_ERR_NULL, "delta is NULL");
+  if (!delta && out->n_tok > 0) return fail(ATTN_ERR_NULL, "delta is NULL");
   DeltaArgs a;
   a.dout = dout->data; a.dtype_do = dout->dtype; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
   a.out = out->data; a.dtype_o = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
@@ -724,7 +724,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
     if (out->n_tok != q->n_tok || out->n_head != q->n_head || out->head_dim != q->head_dim)
       return fail(ATTN_ERR_SHAPE, "out must be shaped like q");
   }
-  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   const attn_tensor *gr[3] = {dq, dk, dv};
   const char *gn[3] = {"dq", "dk", "dv"};
   for (int i = 0; i < 3; ++i) {
@@ -1006,7 +1006,7 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   TRY(check_ring_args(cp, rank, q, k_loc, v_loc));
   if (!dk_loc || !dv_loc) return fail(ATTN_ERR_NULL, "dk_loc/dv_loc is NULL");
   TRY(check_tensor(out, "out"));
-  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (num_seqs < 0 || max_local < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
   if (num_seqs > 0 && !cu) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
   const RingLayout L = ring_layout(q, &k_loc[0], num_seqs);
@@ -1121,7 +1121,7 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
   TRY(attn_kvp_workspace_size(R, q, &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, &need));
   if (!workspace || workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed", need);
   TRY(check_tensor(out, "out"));
-  if (!lse) return fail(ATTN_ERR_NULL, "lse is NULL");
+  if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   char *w = (char *)workspace;
   const size_t obytes = align256((size_t)q->n_tok * q->n_head * q->head_dim * 4);
   const size_t lbytes = align256((size_t)q->n_head * q->n_tok * 4);

@@ -167,7 +167,8 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
  *   q   [n_q, HQ, D]   bf16 or f32
  *   k,v [n_k, HKV, D]  same dtype as q (paged: the cache, see attn_mask)
  *   out [n_q, HQ, D]   bf16 or f32; only rows in the q view are written
- *   lse [HQ, n_q] f32; only rows in the q view are written
+ *   lse [HQ, n_q] f32; only rows in the q view are written (NULL allowed
+ *       when n_q == 0; the same holds for every lse / delta argument below)
  *   scale: multiplies q.k before the softmax (callers pass 1/sqrt(D) for the
  *          pages' default, [ULY] `cached_ulysses_attention` scale)
  * D must be 64 or 128. mask == NULL means full (no causal, all rows).
