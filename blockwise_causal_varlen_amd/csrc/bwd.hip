@@ -402,7 +402,9 @@ __global__ void lse2_kernel(const float *lse, float *lse2, int64_t n) {
   }
 }
 
-template <int D>
+// MASK = false: launches without a causal or window mask (every visible tile is
+// full), whose softmax step then carries no select.
+template <int D, bool MASK>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
@@ -564,7 +566,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
       const int e = j & 3;
       const int c = sub * 32 + 8 * (j >> 2) + e;  // row offset from the lane's first row
       float ex = fast_exp2(__builtin_fmaf(sc[sub][j], sl2, -l4[sub][e]));
-      ex = (uint32_t)(c - mlo) < mspan ? ex : 0.f;
+      if constexpr (MASK) ex = (uint32_t)(c - mlo) < mspan ? ex : 0.f;
       pb[sub][j >> 3][j & 7] = (bf16)ex;
       db[sub][j >> 3][j & 7] = (bf16)(ex * (dpv[sub][j] - d4[sub][e]));
     };
@@ -832,7 +834,12 @@ static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, int whic
     pp.items = a.ksched.items; pp.order = a.ksched.order; pp.count = a.ksched.count;
     const int64_t gk = a.k_items * a.hkv;
     if (gk > 0) {
-      if constexpr (kBf16) hipLaunchKernelGGL((dkdv_bf16_kernel<D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+      if constexpr (kBf16) {
+        if (pp.m.causal || pp.m.window > 0)
+          hipLaunchKernelGGL((dkdv_bf16_kernel<D, true>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+        else
+          hipLaunchKernelGGL((dkdv_bf16_kernel<D, false>), dim3((unsigned)gk), dim3(256), 0, s, pp);
+      }
       else hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3((unsigned)gk), dim3(256), 0, s, pp);
     }
   } else {
