@@ -507,7 +507,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 // barrier per tile. The loop is unrolled by two so that every LDS read names
 // a fixed buffer (the compiler then only waits for the copy at the barrier).
 // ---------------------------------------------------------------------------
-template <int D, typename OutT>
+// MASK = false: launches without a causal or window mask; only the keys past
+// the end of a ragged last tile are masked.
+template <int D, typename OutT, bool MASK>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
@@ -620,7 +622,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
       // (a compile-time constant): compare c with per-lane bounds
       const int32_t lim = nvalid - 4 * g;
       const int32_t t0 = kt - kd0 + 4 * g;
-      if (RR == 0) {
+      if constexpr (!MASK) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            sc[sb][j] = c < lim ? sc[sb][j] : neg_inf();
+          }
+      } else if (RR == 0) {
         const int32_t d = qpos - (koff + t0), dw = d - W;  // causal: c <= d; window: c > d - W
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -766,8 +776,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (out_dtype == 0) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<D, float>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    const bool mask = fp.m.causal || fp.m.window > 0;
+    if (out_dtype == 0) {
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    } else {
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+    }
   } else {
     if (out_dtype == 0)
       hipLaunchKernelGGL((fwd_kernel<T, D, bf16>), dim3((unsigned)grid), dim3(256), 0, s, fp);
