@@ -657,7 +657,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     }
 }
 
-template <int D>
+// MASK = false: launches without a causal or window mask; only the keys past
+// the end of a ragged last tile are masked.
+template <int D, bool MASK>
 __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
@@ -772,7 +774,15 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
       // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
       const int32_t lim = nvalid - 4 * g;
       const int32_t t0 = kt - kd0 + 4 * g;
-      if (RR == 0) {
+      if constexpr (!MASK) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
+            ds[sb][j] = c < lim ? ds[sb][j] : 0.f;
+          }
+      } else if (RR == 0) {
         const int32_t d = qpos - (koff + t0), dw = d - W;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -846,7 +856,12 @@ static hipError_t launch_bwd_t(const BwdParams &base, const BwdArgs &a, int whic
     pp.items = a.qsched.items; pp.order = a.qsched.order; pp.count = a.qsched.count;
     const int64_t gq = a.q_items * a.hq;
     if (gq > 0) {
-      if constexpr (kBf16) hipLaunchKernelGGL((dq_bf16_kernel<D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+      if constexpr (kBf16) {
+        if (pp.m.causal || pp.m.window > 0)
+          hipLaunchKernelGGL((dq_bf16_kernel<D, true>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+        else
+          hipLaunchKernelGGL((dq_bf16_kernel<D, false>), dim3((unsigned)gq), dim3(256), 0, s, pp);
+      }
       else hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)gq), dim3(256), 0, s, pp);
     }
   }
