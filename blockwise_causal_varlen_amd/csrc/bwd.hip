@@ -434,8 +434,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   const WorkItem it = p.items[p.order[rank]];
   // every position and index fits in 32 bits (checked on the host)
   const int32_t q0 = it.q0, q1 = it.q1, qd0 = it.qdoc0, k1 = it.k1, kd0 = it.kdoc0;
-  const int32_t causal = p.m.causal;
-  const int32_t W = (int32_t)p.m.window;
+  const int32_t causal = MASK ? p.m.causal : 0;  // compile-time 0 without a mask
+  const int32_t W = MASK ? (int32_t)p.m.window : 0;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
   const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;
@@ -687,8 +687,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   const WorkItem it = p.items[p.order[rank]];
   // every position and index fits in 32 bits (checked on the host)
   const int32_t q1 = it.q1, k1 = it.k1, kd0 = it.kdoc0;
-  const int32_t causal = p.m.causal;
-  const int32_t W = (int32_t)p.m.window;
+  const int32_t causal = MASK ? p.m.causal : 0;  // compile-time 0 without a mask
+  const int32_t W = MASK ? (int32_t)p.m.window : 0;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
   const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;

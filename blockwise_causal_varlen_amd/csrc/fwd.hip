@@ -542,8 +542,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const WorkItem it = p.items[p.order[rank]];
   // every position and index fits in 32 bits (checked on the host)
   const int32_t k1 = it.k1, kd0 = it.kdoc0, q1 = it.q1;
-  const int32_t causal = p.m.causal;
-  const int32_t W = (int32_t)p.m.window;
+  const int32_t causal = MASK ? p.m.causal : 0;  // compile-time 0 without a mask
+  const int32_t W = MASK ? (int32_t)p.m.window : 0;
   const int32_t qoff = (int32_t)p.m.q_pos_offset;
   const int32_t koff = (int32_t)p.m.pm.k_pos_offset;
   const int32_t RR = p.m.pm.interleave, rr = p.m.pm.rank, SH = p.m.pm.shift;
