@@ -424,6 +424,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < 4);  // 4 waves: lets the copy loops drop their range tests
   const int hkv_count = p.hq / p.group;
   // logical index = (kv head, item): the items of one kv head are neighbours
   const int lb = xcd_block();
@@ -676,6 +677,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < 4);  // 4 waves: lets the copy loops drop their range tests
   // logical index = (kv head, item, head in group), as in the forward
   const int lb = xcd_block();
   const int cap = gridDim.x / p.hq;

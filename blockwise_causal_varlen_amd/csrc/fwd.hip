@@ -530,6 +530,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 5, l32 = lane & 31, u = lane & 15, dh = (lane >> 4) & 1;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < 4);  // 4 waves: lets the copy loops drop their range tests
   // logical index = (kv head, item, head in group): the heads that share a kv
   // head, and the items of one kv head, are neighbours
   const int lb = xcd_block();
