@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     const int32_t dk0 = kp_lane - (qp_lo + 4 * g);
     const int32_t lo = (full || !causal) ? -(1 << 30) : dk0;
     const int32_t hi = (full || W <= 0) ? (1 << 30) : dk0 + W;
-    body(sq, so, sl, sd, lo, (uint32_t)(hi - lo));
+    body(sq, so, sl, sd, lo, (uint32_t)hi - (uint32_t)lo);
   };
 
   if (total > 0) stage(sQ0, sO0, sL0, sD0);
