@@ -101,15 +101,34 @@ class ZigzagWorkload:
             self.q_loc[r], self.dout_loc[r] = q, do
             self.runners[r] = L.RingRunner("zigzag", cp, r, q, self.k_loc, self.v_loc, self.cu_local,
                                            self.max_local, case.scale, dout=do, out_dtype=out_dtype)
+        # Several virtual ranks run at once, each on its own stream (default
+        # priority), as they would on their own GPUs: their inputs are shared
+        # read-only and each writes only its own outputs and workspace.
+        self.streams = ({r: torch.cuda.Stream(device=device) for r in self.ranks}
+                        if len(self.ranks) > 1 else None)
+
+    def _each_rank(self, fn):
+        if self.streams is None:
+            for r in self.ranks:
+                fn(r, None)
+            return
+        cur = torch.cuda.current_stream()
+        for r in self.ranks:
+            self.streams[r].wait_stream(cur)
+        for r in self.ranks:
+            with torch.cuda.stream(self.streams[r]):
+                fn(r, self.streams[r])
+        for r in self.ranks:
+            cur.wait_stream(self.streams[r])
 
     def forward(self):
-        for r in self.ranks:
-            self.runners[r].forward()
+        self._each_rank(lambda r, s: self.runners[r].forward(stream=s))
 
     def backward(self):
-        for r in self.ranks:
+        def bwd(r, s):
             self.runners[r].zero_grads()
-            self.runners[r].backward()
+            self.runners[r].backward(stream=s)
+        self._each_rank(bwd)
 
     def pairs_per_rank(self):
         return zigzag_rank_pairs(self.doc_lens, self.cp)
