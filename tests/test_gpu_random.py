@@ -1,0 +1,111 @@
+"""Seeded random sweep of the block entry points against the fp64 oracle.
+
+Each case draws (from its own seed) document lengths around the tile sizes
+(0, 1, 31..33, 63..65, 127..129, 511..513, ...), query and key sides of equal or
+different lengths, a GQA layout, D = 64 or 128, bf16 or f32, and a random
+combination of causal, sliding window, position offsets, round-robin key
+positions and half views. The forward (out, lse) and the backward (dq, dk, dv,
+with the block's own out and lse as the merged state) are checked element by
+element; rows outside the query view must keep what the caller left there.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from blockwise_causal_varlen_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 256, 300, 511, 513, 1000]
+N_CASES = 40
+SENTINEL_OUT, SENTINEL_LSE = 7.0, 9.0
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def draw(i):
+    """The configuration of case i (its own generator; data comes from inputs)."""
+    rng = np.random.default_rng(1000 + i)
+    nd = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.choice(EDGE_LENS, nd)]
+    klens = lens if rng.random() < 0.5 else [int(x) for x in rng.choice(EDGE_LENS, nd)]
+    hq, hkv = [(4, 1), (4, 2), (2, 2), (8, 2)][int(rng.integers(4))]
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    mk = {}
+    if rng.random() < 0.6:
+        mk["causal"] = True
+        if rng.random() < 0.35:
+            mk["window"] = int(rng.choice([1, 5, 64, 130, 1000]))
+    if rng.random() < 0.2:
+        mk.update(kv_interleave=4, kv_rank=int(rng.integers(4)), block_size=16,
+                  q_pos_offset=int(rng.integers(0, 2000)))
+    elif rng.random() < 0.3:
+        mk.update(q_pos_offset=int(rng.integers(0, 300)), k_pos_offset=int(rng.integers(0, 100)))
+    for side in ("q_view", "k_view"):
+        r = rng.random()
+        if r < 0.2:
+            mk[side] = "front"
+        elif r < 0.4:
+            mk[side] = "back"
+    return lens, klens, hq, hkv, d, dtype, mk
+
+
+def view_rows(cu, view):
+    rows = []
+    for s, e in zip(cu[:-1].tolist(), cu[1:].tolist()):
+        h = (e - s) // 2
+        a, b = (s, e) if view == "all" else ((s, s + h) if view == "front" else (s + h, e))
+        rows.extend(range(a, b))
+    return np.asarray(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_block(gpu_lib, i):
+    L = gpu_lib
+    lens, klens, hq, hkv, d, dtype, mk = draw(i)
+    say(f"case {i}: lens {lens} klens {klens} heads {hq}/{hkv} D={d} {dtype} mask {mk}")
+    g = torch.Generator().manual_seed(2000 + i)
+    cu_q, cu_k = inputs.cu_from_lengths(lens), inputs.cu_from_lengths(klens)
+    nq, nk = int(cu_q[-1]), int(cu_k[-1])
+    q = inputs.normal((nq, hq, d), dtype, g)
+    k = inputs.normal((nk, hkv, d), dtype, g)
+    v = inputs.normal((nk, hkv, d), dtype, g)
+    dout = inputs.normal((nq, hq, d), dtype, g)
+    scale = 1.0 / math.sqrt(d)
+    max_q, max_k = max(lens), max(klens)
+    tol = 2e-2 if dtype == torch.bfloat16 else 1e-4
+    lse_tol = 1e-3 if dtype == torch.bfloat16 else 1e-5
+
+    out = torch.full((nq, hq, d), SENTINEL_OUT, dtype=dtype, device="cuda")
+    lse = torch.full((hq, nq), SENTINEL_LSE, dtype=torch.float32, device="cuda")
+    L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu_q, cu_k, max_q, max_k, scale, L.mask(**mk), out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = O.block_forward(q, k, v, cu_q, cu_k, scale, **mk)
+    rows = view_rows(cu_q, mk.get("q_view", "all"))
+    other = np.setdiff1d(np.arange(nq), rows)
+    go, gl = O.as_f64(out.cpu()), O.as_f64(lse.cpu())
+    assert np.all(go[other] == SENTINEL_OUT) and np.all(gl[:, other] == SENTINEL_LSE), "rows outside the view written"
+    fin = np.isfinite(rl[:, rows])
+    assert np.array_equal(np.isfinite(gl[:, rows]), fin), "-inf pattern of lse differs"
+    e_out = float(np.max(np.abs(go[rows] - ro[rows]), initial=0.0))
+    e_lse = float(np.max(np.abs(gl[:, rows][fin] - rl[:, rows][fin]), initial=0.0))
+    say(f"  fwd: out {e_out:.2e} lse {e_lse:.2e}")
+    assert e_out <= tol and e_lse <= lse_tol, (e_out, e_lse)
+
+    # backward with the block's own (out, lse) as the merged state
+    got = L.block_bwd(dout.cuda(), q.cuda(), k.cuda(), v.cuda(), out, lse, cu_q, cu_k, max_q, max_k, scale,
+                      L.mask(**mk))
+    torch.cuda.synchronize()
+    rb = O.block_backward(dout, q, k, v, out.cpu(), lse.cpu(), cu_q, cu_k, scale, **mk)
+    for name, gt, r in zip(("dq", "dk", "dv"), got, rb):
+        e = float(np.max(np.abs(O.as_f64(gt.cpu()) - r), initial=0.0))
+        big = float(np.max(np.abs(r), initial=0.0))
+        say(f"  {name}: {e:.2e} (max |ref| {big:.2f})")
+        assert e <= max(tol, (2.0 ** -9 if dtype == torch.bfloat16 else 0.0) * big), (name, e)
