@@ -470,15 +470,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
   if (p.segmented) {
-    float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
+    // a row that sees no key of this part writes only its lse (-inf): the
+    // merge of the parts gives the part weight 0 and never reads its out
+    if (lt > 0.f) {
+      float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int d0 = dt * 32 + 8 * j4 + 4 * g;
-        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
-        *reinterpret_cast<float4 *>(po + d0) = v4;
-      }
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int d0 = dt * 32 + 8 * j4 + 4 * g;
+          float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv,
+                       o[dt][4 * j4 + 3] * inv};
+          *reinterpret_cast<float4 *>(po + d0) = v4;
+        }
+    }
     if (g == 0) p.part_lse[((int64_t)it.seg * p.hq + h) * p.n_q + row] = lse_v;
     return;
   }
@@ -715,15 +720,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
   const float lse_v = lt > 0.f ? (mrow + fast_log2(lt)) * kLn2 : neg_inf();
   if (!row_ok) return;
   if (p.segmented) {
-    float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
+    // a row that sees no key of this part writes only its lse (-inf): the
+    // merge of the parts gives the part weight 0 and never reads its out
+    if (lt > 0.f) {
+      float *po = p.part_out + ((int64_t)it.seg * p.n_q + row) * ((int64_t)p.hq * D) + (int64_t)h * D;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const int d0 = dt * 32 + 8 * j4 + 4 * g;
-        float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv, o[dt][4 * j4 + 3] * inv};
-        *reinterpret_cast<float4 *>(po + d0) = v4;
-      }
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const int d0 = dt * 32 + 8 * j4 + 4 * g;
+          float4 v4 = {o[dt][4 * j4] * inv, o[dt][4 * j4 + 1] * inv, o[dt][4 * j4 + 2] * inv,
+                       o[dt][4 * j4 + 3] * inv};
+          *reinterpret_cast<float4 *>(po + d0) = v4;
+        }
+    }
     if (g == 0) p.part_lse[((int64_t)it.seg * p.hq + h) * p.n_q + row] = lse_v;
     return;
   }

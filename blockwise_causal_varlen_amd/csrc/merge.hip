@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void merge_n_kernel(MergeNArgs a) {
         ln = mx + logf(z);
         for (int i = 0; i < a.n_parts; ++i) {
           const float wgt = expf(plse(i) - ln);
-          if (wgt == 0.f) continue;
+          if (wgt == 0.f) continue;  // not read: a forward part that saw no key leaves its out unwritten
           const int pi = a.strided ? 0 : i;
           const int64_t off = a.strided ? i * a.out_stride : 0;
           f32x4 v = a.pdtype[pi] == 0
