@@ -209,8 +209,7 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   P.d = q->head_dim;
   P.paged = m && m->block_table;
   P.n_k_logical = P.paged ? (int64_t)m->max_blocks * m->block_size : k->n_tok;
-  P.nseg = (m && m->seg_size > 0) ? ((int64_t)max_k + m->seg_size - 1) / m->seg_size : 0;
-  if (P.nseg == 0 && m && m->seg_size > 0) P.nseg = 1;
+  P.nseg = 0;
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
   P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
@@ -239,20 +238,39 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
     if ((m->page_stride * esize(k->dtype)) % 16)
       return fail(ATTN_ERR_LAYOUT, "page_stride must be a multiple of 16 bytes");
   }
+  // Parts: each query tile's visible keys are cut into n parts of whole key
+  // tiles, computed as partials and merged. Segments ask for at least as many
+  // parts as max_seqlen_k has segments (so no part is much longer than
+  // seg_size); the cut follows each tile's visible range rather than fixed
+  // segment boundaries, so a window does not leave most parts empty and a few
+  // long (the partition is internal: any one gives the same merged result). A
+  // small grid (the chip holds 512 query-tile workgroups) asks for up to 16
+  // parts of >= 512 keys of max_seqlen_k each.
   P.nsplit = 0;
-  if (allow_split && !P.decode && P.nseg == 0 && max_k >= 1024) {
-    // few query-tile workgroups (the chip holds 512): cut each tile's visible
-    // keys into parts (>= 512 keys of max_k each, at most 16), computed as
-    // segments and merged the same way
-    const int64_t wgs = ((int64_t)P.n_q / kFwdBM + num_seqs) * P.hq;
-    if (wgs > 0 && wgs < 512) {
-      int64_t n = (1024 + wgs - 1) / wgs;
-      if (n > 16) n = 16;
-      if (n > max_k / 512) n = max_k / 512;
-      if (n > 1) {
-        P.nsplit = (int32_t)n;
-        P.nseg = n;
+  if (!P.decode) {
+    int64_t n = 1;
+    if (m && m->seg_size > 0) {
+      int64_t span = max_k;  // keys one query tile can see
+      if (m->window > 0) {
+        const int64_t w = m->window + kFwdBM;
+        const int64_t R = m->kv_interleave;
+        const int64_t vis = R > 0 ? (w + R - 1) / R + 2 * (int64_t)m->block_size : w;
+        if (vis < span) span = vis;
       }
+      n = (span + m->seg_size - 1) / m->seg_size;
+    }
+    if (allow_split && max_k >= 1024) {
+      const int64_t wgs = ((int64_t)P.n_q / kFwdBM + num_seqs) * P.hq;
+      if (wgs > 0 && wgs < 512) {
+        int64_t a = (1024 + wgs - 1) / wgs;
+        if (a > 16) a = 16;
+        if (a > max_k / 512) a = max_k / 512;
+        if (a > n) n = a;
+      }
+    }
+    if (n > 1) {
+      P.nsplit = (int32_t)n;
+      P.nseg = n;
     }
   }
   return check_ranges(q, k, v, m, P.n_k_logical);
@@ -428,6 +446,7 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
   SchedBufs sb = sched_carve(w, cap);
   w += align256(sched_bytes(cap));
   MaskDev md = mask_dev(mask);
+  md.seg_size = 0;  // segments are served by parts of each tile's visible keys (plan_fwd)
   if (pre) {
     if (pre->capacity != cap) return fail(ATTN_ERR_INVALID, "internal: schedule capacity differs");
     sb = *pre;

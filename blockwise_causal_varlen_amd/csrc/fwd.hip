@@ -125,11 +125,7 @@ __device__ void make_item(const SchedParams &p, int64_t qs, int64_t qe, int64_t 
     const int64_t c = ks + m.pm.count_le(m.q_pos_offset + (q0 - qs) - m.window, nk_doc);
     if (c > lo) lo = c;
   }
-  if (m.seg_size > 0) {
-    const int64_t sa = ks + sg * m.seg_size, sbd = sa + m.seg_size;
-    if (sa > lo) lo = sa;
-    if (sbd < hi) hi = sbd;
-  } else if (p.nsplit > 1 && hi > lo) {
+  if (p.nsplit > 1 && hi > lo) {
     // part sg of the visible keys, in whole key tiles
     int64_t chunk = (hi - lo + p.nsplit - 1) / p.nsplit;
     chunk = (chunk + p.key_tile - 1) / p.key_tile * p.key_tile;
@@ -162,8 +158,7 @@ __device__ void sched_run(const SchedParams &p) {
       view_range(qs, qe, m.q_view, qa, qb);
       view_range(ks, ke, m.k_view, ka, kb);
       ntile = p.by_keys ? (kb - ka + p.tile - 1) / p.tile : (qb - qa + p.tile - 1) / p.tile;
-      if (m.seg_size > 0 && !p.by_keys) nseg = (ke - ks + m.seg_size - 1) / m.seg_size;
-      else if (p.nsplit > 1 && !p.by_keys) nseg = p.nsplit;
+      if (p.nsplit > 1 && !p.by_keys) nseg = p.nsplit;
       if (nseg > p.max_seg) nseg = p.max_seg;
       if (nseg < 1) nseg = 1;
     }

@@ -62,7 +62,7 @@ struct SchedJob {
   MaskDev m;
   int32_t tile, key_tile;
   int32_t by_keys;  // 0: tiles of query rows; 1: tiles of key rows (dK/dV)
-  int32_t max_seg;  // segments the partial buffers hold (longer documents are cut)
+  int32_t max_seg;  // parts the partial buffers hold per query tile
   SchedBufs sb;
   int32_t nsplit = 0;  // > 1 (query tiles, no segments): cut each tile's visible keys in nsplit parts
 };

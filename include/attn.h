@@ -118,10 +118,14 @@ typedef struct {
  * stride_tok = elements between rows of a page, stride_head = elements
  * between heads of a page, and page_stride = elements between pages.
  *
- * Segments ([KVP] `seg_size`): seg_size > 0 splits each document's key range
- * into segments of seg_size keys; every (query tile, segment) pair is computed
+ * Segments ([KVP] `seg_size`): seg_size > 0 bounds the keys one partial
+ * covers. Each 128-row query tile's visible keys are cut into n parts of
+ * whole 64-key tiles, n = ceil(keys a tile can see / seg_size) (the keys a
+ * tile can see: max_seqlen_k, or fewer under a window); every part is computed
  * as its own partial (out, lse) in the workspace and the partials are merged
- * in segment order before attn_block_fwd returns.
+ * before attn_block_fwd returns. The cut follows each tile's visible range
+ * rather than fixed segment boundaries; the merged result is the same up to
+ * rounding for any partition.
  */
 typedef struct {
   uint32_t struct_size;   /* must equal sizeof(attn_mask) */
@@ -175,11 +179,12 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
  * Workspace: attn_workspace_size(ATTN_OP_BLOCK_FWD, ...) bytes. It holds,
  * besides the tile schedule: the max_blocks * block_size logical rows of paged
  * K and V (gathered into contiguous rows before the forward; rows of pages
- * outside [0, n_tok / block_size) read as zero); the per-segment partials when
- * seg_size > 0; and, when few 128-row query tiles face many keys (fewer than
- * 512 tile x head workgroups and max_seqlen_k >= 1024, no segments), the
- * partials of each tile's visible keys cut into up to 16 parts, merged like
- * segments. Rows outside the q view stay untouched in every case.
+ * outside [0, n_tok / block_size) read as zero); and the partials of each
+ * query tile's visible keys cut into n parts: the parts seg_size asks for,
+ * and, when few 128-row query tiles face many keys (fewer than 512 tile x
+ * head workgroups and max_seqlen_k >= 1024), up to 16 parts of >= 512 keys
+ * of max_seqlen_k each (the larger count wins; one part needs no partials).
+ * Rows outside the q view stay untouched in every case.
  */
 attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                            const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
