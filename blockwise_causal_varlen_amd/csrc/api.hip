@@ -475,9 +475,8 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     a.part_out = (float *)w;
     w += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
     a.part_lse = (float *)w;
-    // segments no tile reaches must read as empty partials
-    TRY(hip_check(timed("attn_fill", s, [&] { return launch_fill(a.part_lse, P.nseg * P.hq * P.n_q, -INFINITY, s); }),
-                  "fill"));
+    // no fill: every query tile has one item per part, and a part that sees
+    // no key still writes lse = -inf for its rows; rows of no tile are not merged
   }
   TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd(a, s); }), "forward kernel"));
   if (P.nseg > 0) {

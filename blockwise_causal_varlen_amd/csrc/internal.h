@@ -229,6 +229,5 @@ hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int6
                                int64_t heads, int64_t head_dim, const int32_t *cu, int32_t num_seqs,
                                int32_t max_seqlen, int32_t cp, int32_t rank, hipStream_t s);
 
-hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s);
 
 }  // namespace attn

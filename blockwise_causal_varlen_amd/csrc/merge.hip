@@ -521,19 +521,6 @@ hipError_t launch_delta(const DeltaArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ void fill_kernel(float *p, int64_t n, float v) {
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
-}
-
-hipError_t launch_fill(float *p, int64_t n, float v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  int64_t b = (n + 255) / 256;
-  if (b > 8192) b = 8192;
-  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)b), dim3(256), 0, s, p, n, v);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Zig-zag shard (NeMo AutoModel zigzag_ring_attention, module docstring and
 // `get_half_index`): per document of L rows and chunk c = L / (2 cp), local
 // row t of rank r is global row  start + r*c + t            (t <  c)
