@@ -278,13 +278,14 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs) {
+// own_parts = false: the caller provides the key-part partials (block_fwd_impl's PartsOut).
+size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs, bool own_parts = true) {
   if (P.decode)
     return P.dsplit > 1 ? align256((size_t)P.dsplit * P.n_q * P.hq * P.d * 4) + align256((size_t)P.dsplit * P.hq * P.n_q * 4)
                         : 0;
   const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg);
   size_t b = align256(sched_bytes(cap));
-  if (P.nseg > 0) {
+  if (P.nseg > 0 && own_parts) {
     b += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
     b += align256((size_t)P.nseg * P.hq * P.n_q * 4);
   }
@@ -368,6 +369,14 @@ struct FusedMerge {
   int32_t final_view;
 };
 
+// Caller-owned partials: the forward writes its key parts there ([nparts]
+// slices of [n_q, H, D] f32 and [H, n_q] f32; one part when the plan needs
+// none) and leaves the merge to the caller.
+struct PartsOut {
+  float *out, *lse;
+  int64_t nparts;
+};
+
 bool can_fuse_merge(const attn_tensor *q, int32_t max_seqlen_q, const attn_mask *m) {
   return q->dtype == ATTN_BF16 && max_seqlen_q != 1 && !(m && (m->seg_size > 0 || m->block_table));
 }
@@ -377,14 +386,19 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
                            int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
                            const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
                            void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr,
-                           bool allow_split = true) {
+                           bool allow_split = true, const PartsOut *po = nullptr) {
   Problem P;
   TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm));
   TRY(check_out(out, P, "out"));
+  if (po) {
+    if (P.decode || fm) return fail(ATTN_ERR_INVALID, "internal: caller-owned parts need the tiled forward");
+    if (P.nseg == 0) P.nseg = 1;
+    if (P.nseg != po->nparts) return fail(ATTN_ERR_INVALID, "internal: part count differs");
+  }
   if (!lse && P.n_q > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k)) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
   if (!(scale > 0.f) || !isfinite(scale)) return fail(ATTN_ERR_INVALID, "scale must be positive and finite");
-  const size_t need = fwd_ws_bytes(P, num_seqs);
+  const size_t need = fwd_ws_bytes(P, num_seqs, po == nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -471,7 +485,10 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     a.merge = fm->merge ? 1 : 0;
     a.final_view = fm->final_view;
   }
-  if (P.nseg > 0) {
+  if (po) {
+    a.part_out = po->out;
+    a.part_lse = po->lse;
+  } else if (P.nseg > 0) {
     a.part_out = (float *)w;
     w += align256((size_t)P.nseg * P.n_q * P.hq * P.d * 4);
     a.part_lse = (float *)w;
@@ -479,7 +496,7 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     // no key still writes lse = -inf for its rows; rows of no tile are not merged
   }
   TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd(a, s); }), "forward kernel"));
-  if (P.nseg > 0) {
+  if (P.nseg > 0 && !po) {
     MergeNArgs mn{};
     mn.n_parts = (int32_t)P.nseg;
     mn.strided = 1;
@@ -1113,6 +1130,16 @@ attn_status attn_ring_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, con
                       max_seqlen_local, scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream);
 }
 
+// KV-parallel: all R ranks' key parts in one buffer, merged by one pass (the
+// same merge as parts then ranks, one launch instead of R + 1), when that
+// buffer stays within 1 GiB; else each rank merges its parts and the ranks
+// merge after.
+static size_t kvp_parts_bytes(int32_t R, const Problem &P) {
+  const int64_t n = (int64_t)R * (P.nseg > 0 ? P.nseg : 1);
+  return align256((size_t)n * P.n_q * P.hq * P.d * 4) + align256((size_t)n * P.hq * P.n_q * 4);
+}
+static bool kvp_all_parts(int32_t R, const Problem &P) { return kvp_parts_bytes(R, P) <= ((size_t)1 << 30); }
+
 attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
                                     int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, size_t *bytes) {
   if (!bytes) return fail(ATTN_ERR_NULL, "bytes is NULL");
@@ -1120,8 +1147,13 @@ attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_
   Problem P;
   TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
   P.decode = false;
-  const size_t part = align256((size_t)P.n_q * P.hq * P.d * 4) + align256((size_t)P.hq * P.n_q * 4);
-  *bytes = (size_t)R * part + fwd_ws_bytes(P, num_seqs);
+  if (kvp_all_parts(R, P)) {
+    if (P.nseg == 0) P.nseg = 1;
+    *bytes = kvp_parts_bytes(R, P) + fwd_ws_bytes(P, num_seqs, false);
+  } else {
+    const size_t part = align256((size_t)P.n_q * P.hq * P.d * 4) + align256((size_t)P.hq * P.n_q * 4);
+    *bytes = (size_t)R * part + fwd_ws_bytes(P, num_seqs);
+  }
   return ok();
 }
 
@@ -1141,6 +1173,40 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
   TRY(check_tensor(out, "out"));
   if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   char *w = (char *)workspace;
+  Problem P;
+  TRY(plan_fwd(q, &k_caches[0], &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+  P.decode = false;
+  if (kvp_all_parts(R, P)) {
+    const int64_t n = P.nseg > 0 ? P.nseg : 1;
+    const int64_t slice = P.n_q * P.hq * P.d, lslice = P.hq * P.n_q;
+    float *pout = (float *)w;
+    float *plse = (float *)(w + align256((size_t)R * n * slice * 4));
+    const size_t pb = kvp_parts_bytes(R, P);
+    for (int r = 0; r < R; ++r) {
+      attn_mask m = *mask;
+      if (!block_tables[r]) return fail(ATTN_ERR_NULL, "block_tables[%d] is NULL", r);
+      m.block_table = block_tables[r];
+      if (mask->kv_interleave == R) m.kv_rank = r;
+      else m.k_pos_offset = mask->k_pos_offset + (int64_t)r * max_seqlen_k;
+      const PartsOut po{pout + (int64_t)r * n * slice, plse + (int64_t)r * n * lslice, n};
+      TRY(block_fwd_impl(q, &k_caches[r], &v_caches[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
+                         max_seqlen_k, &m, scale, out, lse, w + pb, workspace_bytes - pb, stream, nullptr, nullptr,
+                         true, &po));
+    }
+    if (num_seqs == 0 || P.n_q == 0) return ok();
+    MergeNArgs mn{};
+    mn.n_parts = (int32_t)(R * n);
+    mn.strided = 1;
+    mn.out_stride = slice;
+    mn.lse_stride = lslice;
+    mn.pout[0] = pout; mn.pdtype[0] = ATTN_F32; mn.p_st[0] = P.hq * P.d; mn.p_sh[0] = P.d;
+    mn.plse[0] = plse;
+    mn.out = out->data; mn.out_dtype = out->dtype; mn.o_st = out->stride_tok; mn.o_sh = out->stride_head;
+    mn.lse = lse; mn.n = P.n_q; mn.h = P.hq; mn.d = P.d;
+    mn.cu = cu_seqlens_q; mn.num_seqs = num_seqs; mn.view = (int32_t)mask->q_view;
+    hipStream_t s = (hipStream_t)stream;
+    return hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(mn, s); }), "rank merge");
+  }
   const size_t obytes = align256((size_t)q->n_tok * q->n_head * q->head_dim * 4);
   const size_t lbytes = align256((size_t)q->n_head * q->n_tok * 4);
   std::vector<attn_tensor> parts(R);

@@ -412,8 +412,11 @@ attn_status attn_ring_bwd(int32_t cp, int32_t rank, const attn_tensor *dout,
  *     round robin  (mask->kv_interleave == R): local block b -> global b*R + r
  *     contiguous   (mask->kv_interleave == 0): k_pos_offset = r * max_seqlen_k
  * ([KVP] `kvp_q_offset` = -r * local_kv_len + global_q_offset is the same
- * mask with the offset moved to the query side). The R partials (f32, in the
- * workspace) are merged with attn_merge_n in rank order into out / lse.
+ * mask with the offset moved to the query side). The ranks' key-part
+ * partials (f32, in the workspace) are merged by online softmax into out /
+ * lse in one pass when all of them fit 1 GiB; otherwise each rank merges its
+ * parts and the R rank partials are merged in rank order (same result up to
+ * rounding). Rows outside the q view stay untouched.
  *   k_caches, v_caches  host arrays of R cache descriptors
  *   block_tables        host array of R device pointers (each max_blocks int32)
  *   cu_seqlens_k        logical local key counts per document
