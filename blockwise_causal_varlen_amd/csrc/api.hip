@@ -1139,6 +1139,10 @@ static size_t kvp_parts_bytes(int32_t R, const Problem &P) {
   return align256((size_t)n * P.n_q * P.hq * P.d * 4) + align256((size_t)n * P.hq * P.n_q * 4);
 }
 static bool kvp_all_parts(int32_t R, const Problem &P) { return kvp_parts_bytes(R, P) <= ((size_t)1 << 30); }
+// the R ranks' tile schedules (computed in one launch)
+static size_t kvp_sched_bytes(int32_t R, const Problem &P, int32_t num_seqs) {
+  return (size_t)R * align256(sched_bytes(sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg > 0 ? P.nseg : 1)));
+}
 
 attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
                                     int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, size_t *bytes) {
@@ -1149,7 +1153,7 @@ attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_
   P.decode = false;
   if (kvp_all_parts(R, P)) {
     if (P.nseg == 0) P.nseg = 1;
-    *bytes = kvp_parts_bytes(R, P) + fwd_ws_bytes(P, num_seqs, false);
+    *bytes = kvp_parts_bytes(R, P) + kvp_sched_bytes(R, P, num_seqs) + fwd_ws_bytes(P, num_seqs, false);
   } else {
     const size_t part = align256((size_t)P.n_q * P.hq * P.d * 4) + align256((size_t)P.hq * P.n_q * 4);
     *bytes = (size_t)R * part + fwd_ws_bytes(P, num_seqs);
@@ -1181,17 +1185,40 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
     const int64_t slice = P.n_q * P.hq * P.d, lslice = P.hq * P.n_q;
     float *pout = (float *)w;
     float *plse = (float *)(w + align256((size_t)R * n * slice * 4));
-    const size_t pb = kvp_parts_bytes(R, P);
+    if (P.nseg == 0) P.nseg = 1;
+    const size_t pb = kvp_parts_bytes(R, P), sbb = kvp_sched_bytes(R, P, num_seqs);
+    const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, n);
+    std::vector<attn_mask> mr(R);
+    std::vector<SchedBufs> sbr(R);
     for (int r = 0; r < R; ++r) {
-      attn_mask m = *mask;
+      mr[r] = *mask;
       if (!block_tables[r]) return fail(ATTN_ERR_NULL, "block_tables[%d] is NULL", r);
-      m.block_table = block_tables[r];
-      if (mask->kv_interleave == R) m.kv_rank = r;
-      else m.k_pos_offset = mask->k_pos_offset + (int64_t)r * max_seqlen_k;
+      mr[r].block_table = block_tables[r];
+      if (mask->kv_interleave == R) mr[r].kv_rank = r;
+      else mr[r].k_pos_offset = mask->k_pos_offset + (int64_t)r * max_seqlen_k;
+      sbr[r] = sched_carve(w + pb + (size_t)r * (sbb / R), cap);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (num_seqs > 0 && P.n_q > 0) {
+      // the ranks' schedules (the same as each rank's forward would compute)
+      SchedJob jobs[kMaxSchedJobs];
+      for (int r0 = 0; r0 < R; r0 += kMaxSchedJobs) {
+        const int nj = R - r0 < kMaxSchedJobs ? R - r0 : kMaxSchedJobs;
+        for (int i = 0; i < nj; ++i) {
+          MaskDev md = mask_dev(&mr[r0 + i]);
+          md.seg_size = 0;
+          jobs[i] = SchedJob{cu_seqlens_q, cu_seqlens_k, num_seqs, P.n_q, (int64_t)mask->max_blocks * mask->block_size,
+                             md, kFwdBM, kFwdBN, 0, (int32_t)n, sbr[r0 + i]};
+          jobs[i].nsplit = P.nsplit;
+        }
+        TRY(hip_check(timed("attn_sched", s, [&] { return launch_schedules(jobs, nj, s); }), "scheduler"));
+      }
+    }
+    for (int r = 0; r < R; ++r) {
       const PartsOut po{pout + (int64_t)r * n * slice, plse + (int64_t)r * n * lslice, n};
       TRY(block_fwd_impl(q, &k_caches[r], &v_caches[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
-                         max_seqlen_k, &m, scale, out, lse, w + pb, workspace_bytes - pb, stream, nullptr, nullptr,
-                         true, &po));
+                         max_seqlen_k, &mr[r], scale, out, lse, w + pb + sbb, workspace_bytes - pb - sbb, stream,
+                         nullptr, &sbr[r], true, &po));
     }
     if (num_seqs == 0 || P.n_q == 0) return ok();
     MergeNArgs mn{};
@@ -1204,7 +1231,6 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
     mn.out = out->data; mn.out_dtype = out->dtype; mn.o_st = out->stride_tok; mn.o_sh = out->stride_head;
     mn.lse = lse; mn.n = P.n_q; mn.h = P.hq; mn.d = P.d;
     mn.cu = cu_seqlens_q; mn.num_seqs = num_seqs; mn.view = (int32_t)mask->q_view;
-    hipStream_t s = (hipStream_t)stream;
     return hip_check(timed("attn_merge_n", s, [&] { return launch_merge_n(mn, s); }), "rank merge");
   }
   const size_t obytes = align256((size_t)q->n_tok * q->n_head * q->head_dim * 4);
