@@ -412,23 +412,38 @@ __global__ __launch_bounds__(256) void merge_n_kernel(MergeNArgs a) {
       auto plse = [&](int i) -> float {
         return a.strided ? a.plse[0][li + i * a.lse_stride] : a.plse[i][li];
       };
+      // the G lanes of (row, head) share the parts: lane `sub` reads the lse
+      // of parts sub, sub + G, ...; max and sum are reduced over the group
       float mx = neg_inf();
-      for (int i = 0; i < a.n_parts; ++i) mx = fmaxf(mx, plse(i));
+      for (int i = sub; i < a.n_parts; i += G) mx = fmaxf(mx, plse(i));
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, G));
       f32x4 acc = f32x4{};
       float ln = neg_inf();
       if (mx != neg_inf()) {
         float z = 0.f;
-        for (int i = 0; i < a.n_parts; ++i) z += expf(plse(i) - mx);
+        for (int i = sub; i < a.n_parts; i += G) z += expf(plse(i) - mx);
+#pragma unroll
+        for (int o = G / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, G);
         ln = mx + logf(z);
-        for (int i = 0; i < a.n_parts; ++i) {
-          const float wgt = expf(plse(i) - ln);
-          if (wgt == 0.f) continue;  // not read: a forward part that saw no key leaves its out unwritten
-          const int pi = a.strided ? 0 : i;
-          const int64_t off = a.strided ? i * a.out_stride : 0;
-          f32x4 v = a.pdtype[pi] == 0
-                        ? ld4<bf16>((const bf16 *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub)
-                        : ld4<float>((const float *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub);
-          acc += wgt * v;
+        const int base = threadIdx.x & 63 & ~(G - 1);  // the group's first lane in the wave
+        for (int i0 = 0; i0 < a.n_parts; i0 += G) {
+          const float mine = i0 + sub < a.n_parts ? expf(plse(i0 + sub) - ln) : 0.f;
+          // parts of weight 0 are not read: a forward part that saw no key
+          // leaves its out unwritten
+          uint64_t nz = (__ballot(mine != 0.f) >> base) & (G == 64 ? ~0ull : ((1ull << G) - 1));
+          while (nz) {
+            const int b = __builtin_ctzll(nz);
+            nz &= nz - 1;
+            const float wgt = __shfl(mine, b, G);
+            const int i = i0 + b;
+            const int pi = a.strided ? 0 : i;
+            const int64_t off = a.strided ? i * a.out_stride : 0;
+            f32x4 v = a.pdtype[pi] == 0
+                          ? ld4<bf16>((const bf16 *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub)
+                          : ld4<float>((const float *)a.pout[pi] + off + row * a.p_st[pi] + h * a.p_sh[pi] + 4 * sub);
+            acc += wgt * v;
+          }
         }
       }
       st4<OT>((OT *)a.out + row * a.o_st + h * a.o_sh + 4 * sub, acc);
