@@ -212,15 +212,18 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   P.nseg = 0;
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
-  P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16;
+  // (the decode kernel addresses one sequence's K / V bytes with 32-bit offsets)
+  P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16 &&
+             (int64_t)max_k * (k->stride_tok > v->stride_tok ? k->stride_tok : v->stride_tok) * 2 <
+                 ((int64_t)1 << 31);
   P.dsplit = 1; P.dsplit_len = 0;
   if (P.decode) {
     // flash-decoding split: when the (sequence, kv head) waves cannot fill the
-    // chip, each one's keys are split (>= 256 keys a split, at most 16 splits)
-    // and the partials merged, as segments are
+    // chip (two workgroups of 4 waves a CU), each one's keys are split (>= 256
+    // keys a split, at most 32 splits) and the partials merged, as segments are
     const int64_t waves = (int64_t)num_seqs * P.hkv;
     int64_t n = waves > 0 ? (2048 + waves - 1) / waves : 1;
-    if (n > 16) n = 16;
+    if (n > 32) n = 32;
     if (n > max_k / 256) n = max_k / 256;
     if (n > 1) {
       int64_t len = (max_k + n - 1) / n;

@@ -18,7 +18,8 @@
 //   * stages the V chunk in a wave-private LDS slice and reads V^T operands
 //     with the LDS transpose read, then O^T += V^T P^T.
 // The next chunk's K and V loads are issued before the current chunk is
-// computed, so each wave keeps 16 KB of loads in flight.
+// computed, so each wave keeps 16 KB of loads in flight; at <= 256 registers
+// two workgroups share a CU (32 KB a SIMD in flight).
 #include "internal.h"
 
 namespace attn {
@@ -45,7 +46,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecParams p) {
   constexpr int QD = D / 4;            // head-dim quarter owned by a lane group
   constexpr int NST = QD / 8;          // MFMA k-steps per 16-key tile (4 for D=128)
   constexpr int VP = D + 16;           // LDS pitch of V rows (transpose reads conflict free)
@@ -81,28 +82,37 @@ __global__ __launch_bounds__(256) void decode_kernel(DecParams p) {
       qf[s] = col_ok ? __builtin_bit_cast(bf16x8, ld16(qr + s * 8)) : bf16x8{};
   }
 
-  const bf16 *kbase = p.k + k0 * p.k_st + (int64_t)hk * p.k_sh + g * QD;
-  const bf16 *vbase = p.v + k0 * p.v_st + (int64_t)hk * p.v_sh;
   bf16 *myV = sV[w];
 
-  // chunk loaders (zero beyond the sequence)
+  // K and V of this wave's keys through buffer resources based at its first
+  // key: per-lane byte offsets are fixed, the chunk's offset is a scalar, and
+  // rows past the end read as zero (the host keeps the bytes below 2^31)
+  const int kst = (int)p.k_st, vst = (int)p.v_st;
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.k + k0 * p.k_st + (int64_t)hk * p.k_sh), (short)0,
+                                                     nk > 0 ? (int)(((nk - 1) * p.k_st + D) * 2) : 0, kBufFlags);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(p.v + k0 * p.v_st + (int64_t)hk * p.v_sh), (short)0,
+                                                     nk > 0 ? (int)(((nk - 1) * p.v_st + D) * 2) : 0, kBufFlags);
+  int koff[2][NST], voff[VCH];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < NST; ++s) koff[t][s] = ((t * 16 + u) * kst + g * QD + s * 8) * 2;
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) {
+    const int ci = lane + 64 * c;
+    voff[c] = ((ci / (D / 8)) * vst + (ci % (D / 8)) * 8) * 2;
+  }
   auto load_k = [&](int64_t c0, i32x4 (&kr)[2][NST]) {
+    const int so = (int)c0 * kst * 2;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t key = c0 + t * 16 + u;
-      const bool ok = key < nk;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s = 0; s < NST; ++s) kr[t][s] = ok ? ld16(kbase + key * p.k_st + s * 8) : i32x4{0, 0, 0, 0};
-    }
+      for (int s = 0; s < NST; ++s) kr[t][s] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[t][s], so, 0);
   };
   auto load_v = [&](int64_t c0, i32x4 (&vr)[VCH]) {
+    const int so = (int)c0 * vst * 2;
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int ci = lane + 64 * c;
-      const int kr = ci / (D / 8), col = (ci % (D / 8)) * 8;
-      const int64_t key = c0 + kr;
-      vr[c] = key < nk ? ld16(vbase + key * p.v_st + col) : i32x4{0, 0, 0, 0};
-    }
+    for (int c = 0; c < VCH; ++c) vr[c] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[c], so, 0);
   };
 
   f32x4 o[NDT];
