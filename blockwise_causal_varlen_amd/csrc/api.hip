@@ -1146,6 +1146,10 @@ static bool kvp_all_parts(int32_t R, const Problem &P) { return kvp_parts_bytes(
 static size_t kvp_sched_bytes(int32_t R, const Problem &P, int32_t num_seqs) {
   return (size_t)R * align256(sched_bytes(sched_capacity(P.n_q, num_seqs, kFwdBM, P.nseg > 0 ? P.nseg : 1)));
 }
+// the R ranks' gathered K and V (contiguous logical rows; gathered in one launch)
+static size_t kvp_gather_bytes(int32_t R, const Problem &P) {
+  return (size_t)R * 2 * align256((size_t)P.n_k_logical * P.gather_row_bytes);
+}
 
 attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
                                     int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, size_t *bytes) {
@@ -1154,9 +1158,11 @@ attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_
   Problem P;
   TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
   P.decode = false;
-  if (kvp_all_parts(R, P)) {
+  if (kvp_all_parts(R, P) && P.gather) {
     if (P.nseg == 0) P.nseg = 1;
-    *bytes = kvp_parts_bytes(R, P) + kvp_sched_bytes(R, P, num_seqs) + fwd_ws_bytes(P, num_seqs, false);
+    const size_t g = kvp_gather_bytes(R, P);
+    P.gather = false;  // each rank's forward then runs on its gathered rows
+    *bytes = kvp_parts_bytes(R, P) + kvp_sched_bytes(R, P, num_seqs) + g + fwd_ws_bytes(P, num_seqs, false);
   } else {
     const size_t part = align256((size_t)P.n_q * P.hq * P.d * 4) + align256((size_t)P.hq * P.n_q * 4);
     *bytes = (size_t)R * part + fwd_ws_bytes(P, num_seqs);
@@ -1183,25 +1189,52 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
   Problem P;
   TRY(plan_fwd(q, &k_caches[0], &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
   P.decode = false;
-  if (kvp_all_parts(R, P)) {
+  if (kvp_all_parts(R, P) && P.gather) {
     const int64_t n = P.nseg > 0 ? P.nseg : 1;
     const int64_t slice = P.n_q * P.hq * P.d, lslice = P.hq * P.n_q;
     float *pout = (float *)w;
     float *plse = (float *)(w + align256((size_t)R * n * slice * 4));
     if (P.nseg == 0) P.nseg = 1;
-    const size_t pb = kvp_parts_bytes(R, P), sbb = kvp_sched_bytes(R, P, num_seqs);
+    const size_t pb = kvp_parts_bytes(R, P), sbb = kvp_sched_bytes(R, P, num_seqs), gbb = kvp_gather_bytes(R, P);
+    const size_t gb = gbb / (2 * (size_t)R);
     const int64_t cap = sched_capacity(P.n_q, num_seqs, kFwdBM, n);
+    char *gw = w + pb + sbb;
     std::vector<attn_mask> mr(R);
     std::vector<SchedBufs> sbr(R);
+    std::vector<attn_tensor> kg(R), vg(R);
+    std::vector<PageGatherArgs> ga(R);
     for (int r = 0; r < R; ++r) {
+      const attn_tensor *kc = &k_caches[r], *vc = &v_caches[r];
+      TRY(check_qkv(q, kc, vc));
+      if (kc->n_head != k_caches[0].n_head || kc->dtype != k_caches[0].dtype)
+        return fail(ATTN_ERR_SHAPE, "k_caches[%d] differs from k_caches[0]", r);
+      if (vc->stride_tok != kc->stride_tok || vc->stride_head != kc->stride_head)
+        return fail(ATTN_ERR_LAYOUT, "paged k and v caches must share their strides");
       mr[r] = *mask;
       if (!block_tables[r]) return fail(ATTN_ERR_NULL, "block_tables[%d] is NULL", r);
-      mr[r].block_table = block_tables[r];
       if (mask->kv_interleave == R) mr[r].kv_rank = r;
       else mr[r].k_pos_offset = mask->k_pos_offset + (int64_t)r * max_seqlen_k;
       sbr[r] = sched_carve(w + pb + (size_t)r * (sbb / R), cap);
+      // rank r's logical rows -> contiguous K, V
+      PageGatherArgs &g = ga[r];
+      g.src_k = kc->data; g.src_v = vc->data;
+      g.page_stride = mask->page_stride; g.st = kc->stride_tok; g.sh = kc->stride_head;
+      g.table = block_tables[r]; g.max_blocks = mask->max_blocks; g.n_pages = kc->n_tok / mask->block_size;
+      g.shift = __builtin_ctz((unsigned)mask->block_size);
+      g.dst_k = gw + (size_t)r * 2 * gb; g.dst_v = gw + ((size_t)r * 2 + 1) * gb;
+      g.n_rows = P.n_k_logical; g.h = (int32_t)P.hkv; g.d = (int32_t)P.d; g.eb = esize(kc->dtype);
+      kg[r] = *kc;
+      kg[r].data = g.dst_k; kg[r].n_tok = P.n_k_logical; kg[r].stride_head = P.d; kg[r].stride_tok = P.hkv * P.d;
+      vg[r] = kg[r];
+      vg[r].data = g.dst_v;
+      mr[r].block_table = nullptr; mr[r].max_blocks = 0; mr[r].page_stride = 0;
     }
     hipStream_t s = (hipStream_t)stream;
+    for (int r0 = 0; r0 < R; r0 += kMaxGatherBatch) {
+      const int ng = R - r0 < kMaxGatherBatch ? R - r0 : kMaxGatherBatch;
+      TRY(hip_check(timed("attn_gather", s, [&] { return launch_page_gathers(ga.data() + r0, ng, s); }),
+                    "page gather"));
+    }
     if (num_seqs > 0 && P.n_q > 0) {
       // the ranks' schedules (the same as each rank's forward would compute)
       SchedJob jobs[kMaxSchedJobs];
@@ -1219,9 +1252,9 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
     }
     for (int r = 0; r < R; ++r) {
       const PartsOut po{pout + (int64_t)r * n * slice, plse + (int64_t)r * n * lslice, n};
-      TRY(block_fwd_impl(q, &k_caches[r], &v_caches[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
-                         max_seqlen_k, &mr[r], scale, out, lse, w + pb + sbb, workspace_bytes - pb - sbb, stream,
-                         nullptr, &sbr[r], true, &po));
+      TRY(block_fwd_impl(q, &kg[r], &vg[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, &mr[r],
+                         scale, out, lse, gw + gbb, workspace_bytes - pb - sbb - gbb, stream, nullptr, &sbr[r], true,
+                         &po));
     }
     if (num_seqs == 0 || P.n_q == 0) return ok();
     MergeNArgs mn{};

@@ -153,6 +153,9 @@ struct PageGatherArgs {
   int32_t h, d, eb;
 };
 hipError_t launch_page_gather(const PageGatherArgs &a, hipStream_t s);
+constexpr int kMaxGatherBatch = 16;
+// n (<= kMaxGatherBatch) gathers of equal row counts in one launch
+hipError_t launch_page_gathers(const PageGatherArgs *a, int n, hipStream_t s);
 
 struct DeltaArgs {
   const void *dout; int32_t dtype_do; int64_t do_st, do_sh;

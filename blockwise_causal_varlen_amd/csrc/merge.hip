@@ -590,16 +590,24 @@ hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int6
 // t & (2^shift - 1) of it. One wave copies one logical row (all heads, K and V)
 // into contiguous [rows, H, D] buffers; rows of an invalid page read as zero.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void page_gather_kernel(PageGatherArgs a) {
+__device__ void page_gather_run(const PageGatherArgs &a) {
   const int lane = threadIdx.x & 63;
   const int64_t per_head = (int64_t)a.d * a.eb;
   const int64_t row_bytes = per_head * a.h;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < a.n_rows; t += (int64_t)gridDim.x * 4) {
+  // a row is row_bytes / 16 pieces of 16 bytes; short rows share a wave
+  const int chunks = (int)(row_bytes / 16);
+  int lpr = 64;  // lanes per row
+  while (lpr > 1 && lpr / 2 >= chunks) lpr >>= 1;
+  const int rpw = 64 / lpr;  // rows per wave
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t step = (int64_t)gridDim.x * 4 * rpw;
+  for (int64_t t = wave * rpw + lane / lpr; t < a.n_rows; t += step) {
     const int64_t b = t >> a.shift;
     const int64_t pg = b < a.max_blocks ? a.table[b] : -1;
     const bool ok = pg >= 0 && pg < a.n_pages;
     const int64_t prow = t & ((1 << a.shift) - 1);
-    for (int64_t off = lane * 16; off < row_bytes; off += 64 * 16) {
+    for (int c = lane % lpr; c < chunks; c += lpr) {
+      const int64_t off = (int64_t)c * 16;
       const int64_t hh = off / per_head, dd = off - hh * per_head;
       const int64_t so = (pg * a.page_stride + hh * a.sh + prow * a.st) * a.eb + dd;
       const int64_t dof = t * row_bytes + off;
@@ -614,11 +622,39 @@ __global__ __launch_bounds__(256) void page_gather_kernel(PageGatherArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void page_gather_kernel(PageGatherArgs a) { page_gather_run(a); }
+
+// several gathers (the ranks of a KV-parallel call), grid.y = gather
+struct PageGatherBatch {
+  PageGatherArgs a[kMaxGatherBatch];
+};
+__global__ __launch_bounds__(256) void page_gather_batch_kernel(PageGatherBatch b) { page_gather_run(b.a[blockIdx.y]); }
+
+// workgroups for a gather: 4 waves of rows_per_wave rows each (as page_gather_run)
+static int64_t gather_blocks(const PageGatherArgs &a) {
+  const int chunks = (int)((int64_t)a.d * a.eb * a.h / 16);
+  int lpr = 64;
+  while (lpr > 1 && lpr / 2 >= chunks) lpr >>= 1;
+  const int64_t rows = 4 * (64 / lpr);
+  return (a.n_rows + rows - 1) / rows;
+}
+
 hipError_t launch_page_gather(const PageGatherArgs &a, hipStream_t s) {
   if (a.n_rows <= 0) return hipSuccess;
-  int64_t b = (a.n_rows + 3) / 4;
+  int64_t b = gather_blocks(a);
   if (b > 256 * 16) b = 256 * 16;
   hipLaunchKernelGGL(page_gather_kernel, dim3((unsigned)b), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_gathers(const PageGatherArgs *a, int n, hipStream_t s) {
+  if (n < 1 || n > kMaxGatherBatch) return hipErrorInvalidValue;
+  PageGatherBatch pb{};
+  for (int i = 0; i < n; ++i) pb.a[i] = a[i];
+  if (a[0].n_rows <= 0) return hipSuccess;
+  int64_t b = gather_blocks(a[0]);
+  if (b * n > 256 * 16) b = (256 * 16 + n - 1) / n;
+  hipLaunchKernelGGL(page_gather_batch_kernel, dim3((unsigned)b, (unsigned)n), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 
