@@ -748,7 +748,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            const attn_mask *mask, float scale, const attn_tensor *dq, const attn_tensor *dk,
                            const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream,
-                           const BwdPre *pre) {
+                           const BwdPre *pre, bool set_q = false, bool set_kv = false) {
   TRY(check_qkv(q, k, v));
   TRY(check_mask(mask));
   if (mask && (mask->block_table || mask->seg_size > 0))
@@ -827,6 +827,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
   a.dk = (float *)dk->data; a.dk_st = dk->stride_tok; a.dk_sh = dk->stride_head;
   a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;
   a.qsched = sq; a.ksched = sk; a.q_items = capq; a.k_items = capk;
+  a.set_q = set_q; a.set_kv = set_kv;
   TRY(hip_check(timed("attn_dkdv", s, [&] { return launch_bwd(a, 0, s); }), "dK/dV kernel"));
   return hip_check(timed("attn_dq", s, [&] { return launch_bwd(a, 1, s); }), "dQ kernel");
 }
@@ -1040,7 +1041,7 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
                          const attn_tensor *q, const attn_tensor *k_loc, const attn_tensor *v_loc,
                          const attn_tensor *out, const float *lse, const int32_t *cu, int32_t num_seqs,
                          int32_t max_local, float scale, const attn_tensor *dq, const attn_tensor *dk_loc,
-                         const attn_tensor *dv_loc, void *ws, size_t ws_bytes, void *stream) {
+                         const attn_tensor *dv_loc, void *ws, size_t ws_bytes, void *stream, uint32_t flags = 0) {
   TRY(check_ring_args(cp, rank, q, k_loc, v_loc));
   if (!dk_loc || !dv_loc) return fail(ATTN_ERR_NULL, "dk_loc/dv_loc is NULL");
   TRY(check_tensor(out, "out"));
@@ -1075,10 +1076,36 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
     TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs, 2 * (int)kinds.size(), st); }),
                   "scheduler"));
   }
+  const bool set = (flags & ATTN_BWD_SET) != 0;
+  if (set) {
+    // Every step's source is a different rank, so each block stores its dK / dV
+    // into its owner's buffers, and step 0 (the diagonal block: every row of
+    // every document) stores dq; what no block writes is zeroed here.
+    if (masks[0].q_view != ATTN_VIEW_ALL) return fail(ATTN_ERR_INVALID, "internal: step 0 must see every row");
+    if (2 * cp + 1 > kMaxZeroRows) return fail(ATTN_ERR_UNSUPPORTED, "cp above %d with ATTN_BWD_SET", (kMaxZeroRows - 1) / 2);
+    std::vector<ZeroRows> z;
+    auto zr = [&](const attn_tensor *t, int32_t view) {
+      z.push_back(ZeroRows{(float *)t->data, t->stride_tok, t->stride_head, t->n_tok, (int32_t)t->n_head,
+                           (int32_t)t->head_dim, view});
+    };
+    TRY(check_tensor(dq, "dq"));
+    zr(dq, 0);
+    std::vector<int32_t> view_of(cp, 3);  // never a source: every row
+    for (int s = 0; s < n_steps; ++s) view_of[((rank - s) % cp + cp) % cp] = (int32_t)masks[s].k_view;
+    for (int c = 0; c < cp; ++c) {
+      TRY(check_tensor(&dk_loc[c], "dk_loc"));
+      TRY(check_tensor(&dv_loc[c], "dv_loc"));
+      zr(&dk_loc[c], view_of[c]);
+      zr(&dv_loc[c], view_of[c]);
+    }
+    TRY(hip_check(timed("attn_zero_rows", st, [&] { return launch_zero_rows(z.data(), (int)z.size(), cu, num_seqs, st); }),
+                  "zero rows"));
+  }
   for (int s = 0; s < n_steps; ++s) {
     const int src = ((rank - s) % cp + cp) % cp;
     TRY(block_bwd_impl(dout, q, &k_loc[src], &v_loc[src], out, lse, delta, cu, cu, num_seqs, max_local, max_local,
-                       &masks[s], scale, dq, &dk_loc[src], &dv_loc[src], nullptr, 0, stream, &pre[kind_of[s]]));
+                       &masks[s], scale, dq, &dk_loc[src], &dv_loc[src], nullptr, 0, stream, &pre[kind_of[s]],
+                       set && s == 0, set));
   }
   return ok();
 }
@@ -1110,8 +1137,18 @@ attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, c
                             const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local, float scale,
                             const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc,
                             void *workspace, size_t workspace_bytes, void *stream) {
+  return attn_zigzag_bwd_ex(cp, rank, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs, max_seqlen_local, scale, dq,
+                            dk_loc, dv_loc, workspace, workspace_bytes, stream, 0);
+}
+
+attn_status attn_zigzag_bwd_ex(int32_t cp, int32_t rank, const attn_tensor *dout, const attn_tensor *q,
+                               const attn_tensor *k_loc, const attn_tensor *v_loc, const attn_tensor *out,
+                               const float *lse, const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local,
+                               float scale, const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc,
+                               void *workspace, size_t workspace_bytes, void *stream, uint32_t flags) {
+  if (flags & ~(uint32_t)ATTN_BWD_SET) return fail(ATTN_ERR_INVALID, "unknown flags 0x%x", flags);
   return run_ring_bwd(cp, rank, cp, zigzag_mask, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs, max_seqlen_local,
-                      scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream);
+                      scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream, flags);
 }
 
 attn_status attn_ring_fwd(int32_t cp, int32_t rank, const attn_tensor *q, const attn_tensor *k_loc,
@@ -1128,9 +1165,19 @@ attn_status attn_ring_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, con
                           const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local, float scale,
                           const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc, void *workspace,
                           size_t workspace_bytes, void *stream) {
+  return attn_ring_bwd_ex(cp, rank, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs, max_seqlen_local, scale, dq,
+                          dk_loc, dv_loc, workspace, workspace_bytes, stream, 0);
+}
+
+attn_status attn_ring_bwd_ex(int32_t cp, int32_t rank, const attn_tensor *dout, const attn_tensor *q,
+                             const attn_tensor *k_loc, const attn_tensor *v_loc, const attn_tensor *out,
+                             const float *lse, const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local,
+                             float scale, const attn_tensor *dq, const attn_tensor *dk_loc, const attn_tensor *dv_loc,
+                             void *workspace, size_t workspace_bytes, void *stream, uint32_t flags) {
   if (cp < 1 || rank < 0 || rank >= cp) return fail(ATTN_ERR_INVALID, "need 0 <= rank < cp");
+  if (flags & ~(uint32_t)ATTN_BWD_SET) return fail(ATTN_ERR_INVALID, "unknown flags 0x%x", flags);
   return run_ring_bwd(cp, rank, rank + 1, ring_mask, dout, q, k_loc, v_loc, out, lse, cu_local, num_seqs,
-                      max_seqlen_local, scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream);
+                      max_seqlen_local, scale, dq, dk_loc, dv_loc, workspace, workspace_bytes, stream, flags);
 }
 
 // KV-parallel: all R ranks' key parts in one buffer, merged by one pass (the

@@ -46,6 +46,7 @@ struct BwdParams {
   float *dk; int64_t dk_st, dk_sh;
   float *dv; int64_t dv_st, dv_sh;
   const WorkItem *items; const int32_t *order; const int32_t *count;
+  int32_t set_q, set_kv;  // store dq / dk, dv instead of adding to them
 };
 
 // Row-operand fragment of a 32x32 MFMA from a tile in LDS: lane row `r`, k-step s.
@@ -280,11 +281,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = *reinterpret_cast<float4 *>(dkr + d0);
+      float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      if (!p.set_kv) {
+        a = *reinterpret_cast<float4 *>(dkr + d0);
+        b = *reinterpret_cast<float4 *>(dvr + d0);
+      }
       a.x += p.scale * dk[dt][4 * j4]; a.y += p.scale * dk[dt][4 * j4 + 1];
       a.z += p.scale * dk[dt][4 * j4 + 2]; a.w += p.scale * dk[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dkr + d0) = a;
-      float4 b = *reinterpret_cast<float4 *>(dvr + d0);
       b.x += dv[dt][4 * j4]; b.y += dv[dt][4 * j4 + 1]; b.z += dv[dt][4 * j4 + 2]; b.w += dv[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dvr + d0) = b;
     }
@@ -383,7 +387,8 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = *reinterpret_cast<float4 *>(dqr + d0);
+      float4 a = {0.f, 0.f, 0.f, 0.f};
+      if (!p.set_q) a = *reinterpret_cast<float4 *>(dqr + d0);
       a.x += p.scale * dq[dt][4 * j4]; a.y += p.scale * dq[dt][4 * j4 + 1];
       a.z += p.scale * dq[dt][4 * j4 + 2]; a.w += p.scale * dq[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dqr + d0) = a;
@@ -648,11 +653,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = *reinterpret_cast<float4 *>(dkr + d0);
+      float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+      if (!p.set_kv) {
+        a = *reinterpret_cast<float4 *>(dkr + d0);
+        b = *reinterpret_cast<float4 *>(dvr + d0);
+      }
       a.x += p.scale * dk[dt][4 * j4]; a.y += p.scale * dk[dt][4 * j4 + 1];
       a.z += p.scale * dk[dt][4 * j4 + 2]; a.w += p.scale * dk[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dkr + d0) = a;
-      float4 b = *reinterpret_cast<float4 *>(dvr + d0);
       b.x += dv[dt][4 * j4]; b.y += dv[dt][4 * j4 + 1]; b.z += dv[dt][4 * j4 + 2]; b.w += dv[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dvr + d0) = b;
     }
@@ -831,7 +839,8 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = *reinterpret_cast<float4 *>(dqr + d0);
+      float4 a = {0.f, 0.f, 0.f, 0.f};
+      if (!p.set_q) a = *reinterpret_cast<float4 *>(dqr + d0);
       a.x += p.scale * dq[dt][4 * j4]; a.y += p.scale * dq[dt][4 * j4 + 1];
       a.z += p.scale * dq[dt][4 * j4 + 2]; a.w += p.scale * dq[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dqr + d0) = a;
@@ -883,6 +892,8 @@ hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   p.dq = a.dq; p.dq_st = a.dq_st; p.dq_sh = a.dq_sh;
   p.dk = a.dk; p.dk_st = a.dk_st; p.dk_sh = a.dk_sh;
   p.dv = a.dv; p.dv_st = a.dv_st; p.dv_sh = a.dv_sh;
+  p.set_q = a.set_q ? 1 : 0;
+  p.set_kv = a.set_kv ? 1 : 0;
   if (a.dtype == 0) {
     if (a.head_dim == 128) return launch_bwd_t<bf16, 128>(p, a, which, s);
     return launch_bwd_t<bf16, 64>(p, a, which, s);

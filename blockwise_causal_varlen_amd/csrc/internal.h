@@ -223,9 +223,21 @@ struct BwdArgs {
   SchedBufs qsched;   // tiles of query rows (dQ kernel)
   SchedBufs ksched;   // tiles of key rows (dK/dV kernel)
   int64_t q_items, k_items;
+  bool set_q = false, set_kv = false;  // store the gradients instead of adding to them
 };
 hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s);
 hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s);  // 0: dK/dV, 1: dQ
+
+// Zero the rows of an f32 [n, h, d] tensor that a block with this view does
+// not write: rows outside every document, and (view 1 / 2) the back / front
+// half of each document; view 3: every row.
+struct ZeroRows {
+  float *t;
+  int64_t st, sh, n;
+  int32_t h, d, view;
+};
+constexpr int kMaxZeroRows = 40;
+hipError_t launch_zero_rows(const ZeroRows *a, int n, const int32_t *cu, int32_t num_seqs, hipStream_t s);
 
 hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int64_t n_src, void *dst,
                                int64_t d_st, int64_t d_sh, int64_t n_dst, int32_t elem_bytes,

@@ -630,6 +630,67 @@ struct PageGatherBatch {
 };
 __global__ __launch_bounds__(256) void page_gather_batch_kernel(PageGatherBatch b) { page_gather_run(b.a[blockIdx.y]); }
 
+// ---------------------------------------------------------------------------
+// Zero the gradient rows a backward that stores (instead of adding) does not
+// write. grid.y = tensor; a workgroup takes 64 rows at a time, 16-byte stores.
+struct ZeroRowsBatch {
+  ZeroRows a[kMaxZeroRows];
+  const int32_t *cu;
+  int32_t num_seqs;
+};
+
+// row is written by a block with this view: inside a document, in the view
+__device__ __forceinline__ bool row_covered(const int32_t *cu, int32_t num_seqs, int view, int64_t row) {
+  if (view == 3 || num_seqs <= 0 || row < cu[0] || row >= cu[num_seqs]) return false;
+  return view == 0 || row_in_view(cu, num_seqs, view, row);
+}
+
+constexpr int kZeroRowsChunk = 64;  // rows a workgroup decides at once (one per lane of wave 0)
+
+__global__ __launch_bounds__(256) void zero_rows_kernel(ZeroRowsBatch b) {
+  const ZeroRows &a = b.a[blockIdx.y];
+  const int per_row = a.h * a.d / 4;  // float4 pieces
+  __shared__ int32_t s_zero[kZeroRowsChunk];
+  __shared__ int32_t s_any;
+  for (int64_t r0 = (int64_t)blockIdx.x * kZeroRowsChunk; r0 < a.n; r0 += (int64_t)gridDim.x * kZeroRowsChunk) {
+    // the lanes of wave 0 search their rows' documents side by side
+    if (threadIdx.x < kZeroRowsChunk) {
+      const int64_t row = r0 + threadIdx.x;
+      const bool z = row < a.n && !row_covered(b.cu, b.num_seqs, a.view, row);
+      s_zero[threadIdx.x] = z ? 1 : 0;
+      const unsigned long long any = __ballot(z);
+      if (threadIdx.x == 0) s_any = any != 0ull ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_any) {
+      for (int j = threadIdx.x; j < kZeroRowsChunk * per_row; j += 256) {
+        const int rr = j / per_row, pc = j - rr * per_row;
+        if (!s_zero[rr]) continue;
+        const int hh = (4 * pc) / a.d, dd = 4 * pc - hh * a.d;
+        *reinterpret_cast<float4 *>(a.t + (r0 + rr) * a.st + hh * a.sh + dd) = float4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_zero_rows(const ZeroRows *a, int n, const int32_t *cu, int32_t num_seqs, hipStream_t s) {
+  if (n < 1 || n > kMaxZeroRows) return hipErrorInvalidValue;
+  ZeroRowsBatch zb{};
+  int64_t rows = 0;
+  for (int i = 0; i < n; ++i) {
+    zb.a[i] = a[i];
+    if (a[i].n > rows) rows = a[i].n;
+  }
+  zb.cu = cu;
+  zb.num_seqs = num_seqs;
+  if (rows <= 0) return hipSuccess;
+  int64_t g = (rows + kZeroRowsChunk - 1) / kZeroRowsChunk;
+  if (g > 2048) g = 2048;
+  hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)g, (unsigned)n), dim3(256), 0, s, zb);
+  return hipGetLastError();
+}
+
 // workgroups for a gather: 4 waves of rows_per_wave rows each (as page_gather_run)
 static int64_t gather_blocks(const PageGatherArgs &a) {
   const int chunks = (int)((int64_t)a.d * a.eb * a.h / 16);

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 BF16, F32 = 0, 1
 VIEW_ALL, VIEW_FRONT, VIEW_BACK = 0, 1, 2
 OP_BLOCK_FWD, OP_BLOCK_BWD = 0, 1
+BWD_SET = 1  # ATTN_BWD_SET: the backward drivers set the gradients instead of adding to them
 _VIEWS = {"all": VIEW_ALL, "front": VIEW_FRONT, "back": VIEW_BACK}
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_DTYPE", 3: "ATTN_ERR_SHAPE", 4: "ATTN_ERR_GQA",
           5: "ATTN_ERR_CU_SEQLENS", 6: "ATTN_ERR_LAYOUT", 7: "ATTN_ERR_UNSUPPORTED", 8: "ATTN_ERR_WORKSPACE",
@@ -76,8 +77,10 @@ _SIGS = {
     "attn_zigzag_workspace_size": (C.c_int, [I32, T, T, I32, I32, C.POINTER(SZ)]),
     "attn_zigzag_fwd": (C.c_int, [I32, I32, T, T, T, P, I32, I32, F, T, T, P, P, SZ, P]),
     "attn_zigzag_bwd": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P]),
+    "attn_zigzag_bwd_ex": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P, C.c_uint32]),
     "attn_ring_fwd": (C.c_int, [I32, I32, T, T, T, P, I32, I32, F, T, T, P, P, SZ, P]),
     "attn_ring_bwd": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P]),
+    "attn_ring_bwd_ex": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P, C.c_uint32]),
     "attn_kvp_workspace_size": (C.c_int, [I32, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
     "attn_kvp_fwd": (C.c_int, [I32, T, T, T, C.POINTER(P), P, P, I32, I32, I32, M, F, T, P, P, SZ, P]),
     "attn_validate_inputs": (C.c_int, [T, T, P, P, I32, I32, I32, M, I32, I32, P]),
@@ -387,12 +390,14 @@ class RingRunner:
         for t in self.dk + self.dv:
             t.zero_()
 
-    def backward(self, stream=None):
-        name = "attn_zigzag_bwd" if self.kind == "zigzag" else "attn_ring_bwd"
+    def backward(self, stream=None, set_grads=False):
+        """Gradients into dq / dk / dv: added to them, or (set_grads) set, with
+        no zeroing needed first (ATTN_BWD_SET)."""
+        name = "attn_zigzag_bwd_ex" if self.kind == "zigzag" else "attn_ring_bwd_ex"
         _call(name, self.cp, self.rank, C.byref(self.dod), C.byref(self.qd), self.kd, self.vd,
               C.byref(self.bwd_od if self.bwd_od is not None else self.od),
               self.lse.data_ptr(), self.cu.data_ptr(), self.ns, self.max_local, self.scale, C.byref(self.dqd),
-              self.dkd, self.dvd, self.wp, self.wn, _stream(stream))
+              self.dkd, self.dvd, self.wp, self.wn, _stream(stream), BWD_SET if set_grads else 0)
         return self.dq, self.dk, self.dv
 
 

@@ -125,10 +125,8 @@ class ZigzagWorkload:
         self._each_rank(lambda r, s: self.runners[r].forward(stream=s))
 
     def backward(self):
-        def bwd(r, s):
-            self.runners[r].zero_grads()
-            self.runners[r].backward(stream=s)
-        self._each_rank(bwd)
+        # the drivers store the gradients (no zeroing pass needed first)
+        self._each_rank(lambda r, s: self.runners[r].backward(stream=s, set_grads=True))
 
     def pairs_per_rank(self):
         return zigzag_rank_pairs(self.doc_lens, self.cp)
@@ -189,8 +187,7 @@ class EagleWorkload:
         sc = self.case.base.scale
         for r in self.ranks:
             run = self.zz.runners[r]
-            run.zero_grads()
-            run.backward()  # block 0 with the final merged out and lse
+            run.backward(set_grads=True)  # block 0 with the final merged out and lse
             L.bwd_delta(self.zz.dout_loc[r], self.final[r], delta=self.delta[r])
             for i in range(self.n_ttt):
                 self.dtk[r][i].zero_()

@@ -383,6 +383,29 @@ attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout,
                             void *stream);
 
 /*
+ * Backward driver flags (attn_zigzag_bwd_ex, attn_ring_bwd_ex; 0 = the
+ * accumulating attn_zigzag_bwd / attn_ring_bwd).
+ *   ATTN_BWD_SET: the call SETS dq and every dk_loc[c] / dv_loc[c] instead of
+ *   adding to them, so the caller need not zero them first (the pages'
+ *   backward starts from fresh zero buffers each call). Each step's source
+ *   is a different rank, so each block stores its dk/dv into its owner's
+ *   buffers; step 0 (the diagonal block, every row of every document) stores
+ *   dq and later steps add; rows no block writes (the other half of a
+ *   half-view source, sources no step uses, rows outside every document) are
+ *   written as zeros. Results equal the accumulating call on zeroed buffers
+ *   exactly. cp <= 19 with this flag (ATTN_ERR_UNSUPPORTED beyond).
+ * Unknown flag bits: ATTN_ERR_INVALID.
+ */
+#define ATTN_BWD_SET 1u
+attn_status attn_zigzag_bwd_ex(int32_t cp, int32_t rank, const attn_tensor *dout,
+                               const attn_tensor *q, const attn_tensor *k_loc,
+                               const attn_tensor *v_loc, const attn_tensor *out, const float *lse,
+                               const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local,
+                               float scale, const attn_tensor *dq, const attn_tensor *dk_loc,
+                               const attn_tensor *dv_loc, void *workspace, size_t workspace_bytes,
+                               void *stream, uint32_t flags);
+
+/*
  * attn_ring_fwd / attn_ring_bwd -- contiguous ring, causal ([RING]
  * `ring_flash_attn_forward` / `ring_flash_attn_backward`): rank r attends the
  * K/V of steps s <= r (src = r - s), causal only at s == 0. Arguments as for
@@ -400,6 +423,13 @@ attn_status attn_ring_bwd(int32_t cp, int32_t rank, const attn_tensor *dout,
                           float scale, const attn_tensor *dq, const attn_tensor *dk_loc,
                           const attn_tensor *dv_loc, void *workspace, size_t workspace_bytes,
                           void *stream);
+attn_status attn_ring_bwd_ex(int32_t cp, int32_t rank, const attn_tensor *dout,
+                             const attn_tensor *q, const attn_tensor *k_loc,
+                             const attn_tensor *v_loc, const attn_tensor *out, const float *lse,
+                             const int32_t *cu_local, int32_t num_seqs, int32_t max_seqlen_local,
+                             float scale, const attn_tensor *dq, const attn_tensor *dk_loc,
+                             const attn_tensor *dv_loc, void *workspace, size_t workspace_bytes,
+                             void *stream, uint32_t flags);
 
 /*
  * attn_kvp_fwd -- KV-parallel segmented prefill over R virtual ranks ([KVP]
