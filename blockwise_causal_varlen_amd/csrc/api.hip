@@ -748,7 +748,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
                            const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            const attn_mask *mask, float scale, const attn_tensor *dq, const attn_tensor *dk,
                            const attn_tensor *dv, void *workspace, size_t workspace_bytes, void *stream,
-                           const BwdPre *pre, bool set_q = false, bool set_kv = false) {
+                           const BwdPre *pre, bool set_q = false, bool set_kv = false, bool check_only = false) {
   TRY(check_qkv(q, k, v));
   TRY(check_mask(mask));
   if (mask && (mask->block_table || mask->seg_size > 0))
@@ -790,7 +790,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
     if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
   hipStream_t s = (hipStream_t)stream;
-  if (num_seqs == 0 || q->n_tok == 0 || k->n_tok == 0) return ok();
+  if (check_only || num_seqs == 0 || q->n_tok == 0 || k->n_tok == 0) return ok();
 
   MaskDev md = mask_dev(mask);
   SchedBufs sq, sk;
@@ -1054,36 +1054,19 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   char *w = (char *)ws;
   float *delta = (float *)(w + L.delta_off);
   float *lse2 = (float *)(w + L.lse2_off);
-  TRY(attn_bwd_delta(dout, out, delta, stream));
   hipStream_t st = (hipStream_t)stream;
   std::vector<attn_mask> masks, kinds;
   std::vector<int> kind_of;
   TRY(ring_kinds(cp, rank, n_steps, mk, masks, kind_of, kinds));
-  std::vector<BwdPre> pre(kinds.size());
-  if (num_seqs > 0 && q->n_tok > 0) {
-    TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st); }), "lse2"));
-    SchedJob jobs[2 * kRingKinds];
-    for (size_t i = 0; i < kinds.size(); ++i) {
-      TRY(check_mask(&kinds[i]));
-      char *b = w + L.bsched_off + i * L.bsched_stride;
-      pre[i].sq = sched_carve(b, L.qcap);
-      pre[i].sk = sched_carve(b + align256(sched_bytes(L.qcap)), L.kcap);
-      pre[i].lse2 = lse2;
-      const MaskDev md = mask_dev(&kinds[i]);
-      jobs[2 * i] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kFwdBN, 0, 1, pre[i].sq};
-      jobs[2 * i + 1] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kBwdBQ, 1, 1, pre[i].sk};
-    }
-    TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs, 2 * (int)kinds.size(), st); }),
-                  "scheduler"));
-  }
+  for (size_t i = 0; i < kinds.size(); ++i) TRY(check_mask(&kinds[i]));
   const bool set = (flags & ATTN_BWD_SET) != 0;
+  std::vector<ZeroRows> z;
   if (set) {
     // Every step's source is a different rank, so each block stores its dK / dV
     // into its owner's buffers, and step 0 (the diagonal block: every row of
-    // every document) stores dq; what no block writes is zeroed here.
+    // every document) stores dq; what no block writes is zeroed before them.
     if (masks[0].q_view != ATTN_VIEW_ALL) return fail(ATTN_ERR_INVALID, "internal: step 0 must see every row");
     if (2 * cp + 1 > kMaxZeroRows) return fail(ATTN_ERR_UNSUPPORTED, "cp above %d with ATTN_BWD_SET", (kMaxZeroRows - 1) / 2);
-    std::vector<ZeroRows> z;
     auto zr = [&](const attn_tensor *t, int32_t view) {
       z.push_back(ZeroRows{(float *)t->data, t->stride_tok, t->stride_head, t->n_tok, (int32_t)t->n_head,
                            (int32_t)t->head_dim, view});
@@ -1098,6 +1081,32 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
       zr(&dk_loc[c], view_of[c]);
       zr(&dv_loc[c], view_of[c]);
     }
+  }
+  const BwdPre none{};
+  for (int s = 0; s < n_steps; ++s) {  // every block's arguments, before anything is launched
+    const int src = ((rank - s) % cp + cp) % cp;
+    TRY(block_bwd_impl(dout, q, &k_loc[src], &v_loc[src], out, lse, delta, cu, cu, num_seqs, max_local, max_local,
+                       &masks[s], scale, dq, &dk_loc[src], &dv_loc[src], nullptr, 0, stream, &none, false, false,
+                       true));
+  }
+  TRY(attn_bwd_delta(dout, out, delta, stream));
+  std::vector<BwdPre> pre(kinds.size());
+  if (num_seqs > 0 && q->n_tok > 0) {
+    TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st); }), "lse2"));
+    SchedJob jobs[2 * kRingKinds];
+    for (size_t i = 0; i < kinds.size(); ++i) {
+      char *b = w + L.bsched_off + i * L.bsched_stride;
+      pre[i].sq = sched_carve(b, L.qcap);
+      pre[i].sk = sched_carve(b + align256(sched_bytes(L.qcap)), L.kcap);
+      pre[i].lse2 = lse2;
+      const MaskDev md = mask_dev(&kinds[i]);
+      jobs[2 * i] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kFwdBN, 0, 1, pre[i].sq};
+      jobs[2 * i + 1] = SchedJob{cu, cu, num_seqs, q->n_tok, k_loc[0].n_tok, md, kBwdTile, kBwdBQ, 1, 1, pre[i].sk};
+    }
+    TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs, 2 * (int)kinds.size(), st); }),
+                  "scheduler"));
+  }
+  if (set) {
     TRY(hip_check(timed("attn_zero_rows", st, [&] { return launch_zero_rows(z.data(), (int)z.size(), cu, num_seqs, st); }),
                   "zero rows"));
   }

@@ -138,3 +138,28 @@ def test_binding_refuses_to_run_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         L.load()
+
+
+def test_backward_driver_flags(so):
+    """attn_*_bwd_ex: unknown flag bits, the cp limit of ATTN_BWD_SET and a bad
+    gradient shape are refused before anything is launched (no GPU here, so a
+    launch would have reported ATTN_ERR_HIP instead)."""
+    lib = L.load()
+
+    def call(fn, cp, flags, dk_bad=False):
+        kv = (L.AttnTensor * cp)(*[T(h=2) for _ in range(cp)])
+        gs = [T(h=2, dtype=L.F32) for _ in range(cp)]
+        if dk_bad:
+            gs[0] = T(n=63, h=2, dtype=L.F32)  # rank 0 uses source 0 in both rings
+        g = (L.AttnTensor * cp)(*gs)
+        gv = (L.AttnTensor * cp)(*[T(h=2, dtype=L.F32) for _ in range(cp)])
+        return getattr(lib, fn)(cp, 0, C.byref(T()), C.byref(T()), kv, kv, C.byref(T()), FAKE, FAKE, 1, 64, 0.1,
+                                C.byref(T(dtype=L.F32)), g, gv, FAKE, 1 << 30, None, flags)
+
+    for fn in ("attn_zigzag_bwd_ex", "attn_ring_bwd_ex"):
+        assert call(fn, 2, 2) == 11                                # unknown flag bit
+        assert call(fn, 2, 1 | 4) == 11
+        assert call(fn, 2, L.BWD_SET, dk_bad=True) == 3            # dk of one owner misshaped
+        assert call(fn, 2, 0, dk_bad=True) == 3
+    assert call("attn_zigzag_bwd_ex", 20, L.BWD_SET) == 7          # 2 cp + 1 buffers beyond the zeroing launch
+    assert "ATTN_BWD_SET" in L.attn_last_error()
