@@ -1071,13 +1071,21 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
       z.push_back(ZeroRows{(float *)t->data, t->stride_tok, t->stride_head, t->n_tok, (int32_t)t->n_head,
                            (int32_t)t->head_dim, view});
     };
-    TRY(check_tensor(dq, "dq"));
+    // the zeroing writes f32 rows of every buffer, used by a block or not
+    auto like = [&](const attn_tensor *t, const attn_tensor *ref, const char *name) -> attn_status {
+      TRY(check_tensor(t, name));
+      if (t->dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "%s must be f32", name);
+      if (t->n_tok != ref->n_tok || t->n_head != ref->n_head || t->head_dim != ref->head_dim)
+        return fail(ATTN_ERR_SHAPE, "%s must be shaped like its tensor", name);
+      return ok();
+    };
+    TRY(like(dq, q, "dq"));
     zr(dq, 0);
     std::vector<int32_t> view_of(cp, 3);  // never a source: every row
     for (int s = 0; s < n_steps; ++s) view_of[((rank - s) % cp + cp) % cp] = (int32_t)masks[s].k_view;
     for (int c = 0; c < cp; ++c) {
-      TRY(check_tensor(&dk_loc[c], "dk_loc"));
-      TRY(check_tensor(&dv_loc[c], "dv_loc"));
+      TRY(like(&dk_loc[c], &k_loc[c], "dk_loc"));
+      TRY(like(&dv_loc[c], &v_loc[c], "dv_loc"));
       zr(&dk_loc[c], view_of[c]);
       zr(&dv_loc[c], view_of[c]);
     }

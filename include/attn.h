@@ -393,7 +393,10 @@ attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout,
  *   dq and later steps add; rows no block writes (the other half of a
  *   half-view source, sources no step uses, rows outside every document) are
  *   written as zeros. Results equal the accumulating call on zeroed buffers
- *   exactly. cp <= 19 with this flag (ATTN_ERR_UNSUPPORTED beyond).
+ *   exactly. cp <= 19 with this flag (ATTN_ERR_UNSUPPORTED beyond). Every
+ *   dk_loc[c] / dv_loc[c], also of a source the rank never uses, is written,
+ *   so each must be f32 and shaped like k_loc[c] (ATTN_ERR_DTYPE /
+ *   ATTN_ERR_SHAPE), checked before anything is launched.
  * Unknown flag bits: ATTN_ERR_INVALID.
  */
 #define ATTN_BWD_SET 1u

@@ -161,5 +161,12 @@ def test_backward_driver_flags(so):
         assert call(fn, 2, 1 | 4) == 11
         assert call(fn, 2, L.BWD_SET, dk_bad=True) == 3            # dk of one owner misshaped
         assert call(fn, 2, 0, dk_bad=True) == 3
+    # ring rank 0 uses only source 0, but stored mode zeroes source 1's buffers too
+    kv = (L.AttnTensor * 2)(T(h=2), T(h=2))
+    for bad, code in ((T(h=2), 2), (T(n=65, h=2, dtype=L.F32), 3)):
+        g = (L.AttnTensor * 2)(T(h=2, dtype=L.F32), bad)
+        gv = (L.AttnTensor * 2)(T(h=2, dtype=L.F32), T(h=2, dtype=L.F32))
+        assert lib.attn_ring_bwd_ex(2, 0, C.byref(T()), C.byref(T()), kv, kv, C.byref(T()), FAKE, FAKE, 1, 64, 0.1,
+                                    C.byref(T(dtype=L.F32)), g, gv, FAKE, 1 << 30, None, L.BWD_SET) == code
     assert call("attn_zigzag_bwd_ex", 20, L.BWD_SET) == 7          # 2 cp + 1 buffers beyond the zeroing launch
     assert "ATTN_BWD_SET" in L.attn_last_error()
