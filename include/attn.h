@@ -386,8 +386,9 @@ attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout,
  * Backward driver flags (attn_zigzag_bwd_ex, attn_ring_bwd_ex; 0 = the
  * accumulating attn_zigzag_bwd / attn_ring_bwd).
  *   ATTN_BWD_SET: the call SETS dq and every dk_loc[c] / dv_loc[c] instead of
- *   adding to them, so the caller need not zero them first (the pages'
- *   backward starts from fresh zero buffers each call). Each step's source
+ *   adding to them, so the caller need not zero them first ([RING]
+ *   `ring_flash_attn_backward` starts its gradient buffers at zero on every
+ *   call; this gives the same result without a separate zeroing pass). Each step's source
  *   is a different rank, so each block stores its dk/dv into its owner's
  *   buffers; step 0 (the diagonal block, every row of every document) stores
  *   dq and later steps add; rows no block writes (the other half of a
