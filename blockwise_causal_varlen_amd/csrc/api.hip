@@ -389,7 +389,7 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
                            int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
                            const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
                            void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr,
-                           bool allow_split = true, const PartsOut *po = nullptr) {
+                           bool allow_split = true, const PartsOut *po = nullptr, FwdArgs *defer = nullptr) {
   Problem P;
   TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm));
   TRY(check_out(out, P, "out"));
@@ -497,6 +497,11 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     a.part_lse = (float *)w;
     // no fill: every query tile has one item per part, and a part that sees
     // no key still writes lse = -inf for its rows; rows of no tile are not merged
+  }
+  if (defer) {  // the caller launches it with others (writes to the given parts only)
+    if (!po) return fail(ATTN_ERR_INVALID, "internal: a deferred forward needs its parts buffer");
+    *defer = a;
+    return ok();
   }
   TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd(a, s); }), "forward kernel"));
   if (P.nseg > 0 && !po) {
@@ -1314,11 +1319,26 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
         TRY(hip_check(timed("attn_sched", s, [&] { return launch_schedules(jobs, nj, s); }), "scheduler"));
       }
     }
+    // the ranks' forwards: one launch when their shapes agree (each alone is
+    // often too small to fill the chip), else one launch each
+    std::vector<FwdArgs> fa(R);
     for (int r = 0; r < R; ++r) {
       const PartsOut po{pout + (int64_t)r * n * slice, plse + (int64_t)r * n * lslice, n};
       TRY(block_fwd_impl(q, &kg[r], &vg[r], cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, &mr[r],
                          scale, out, lse, gw + gbb, workspace_bytes - pb - sbb - gbb, stream, nullptr, &sbr[r], true,
-                         &po));
+                         &po, &fa[r]));
+    }
+    if (num_seqs > 0 && P.n_q > 0) {
+      for (int r0 = 0; r0 < R; r0 += kMaxFwdBatch) {
+        const int nb = R - r0 < kMaxFwdBatch ? R - r0 : kMaxFwdBatch;
+        if (fwd_batchable(fa.data() + r0, nb)) {
+          TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd_batch(fa.data() + r0, nb, s); }),
+                        "forward kernel"));
+        } else {
+          for (int r = r0; r < r0 + nb; ++r)
+            TRY(hip_check(timed("attn_fwd", s, [&] { return launch_fwd(fa[r], s); }), "forward kernel"));
+        }
+      }
     }
     if (num_seqs == 0 || P.n_q == 0) return ok();
     MergeNArgs mn{};

@@ -502,6 +502,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// several forwards of one shape in one launch (grid.y = which), e.g. the
+// KV-parallel ranks, each too small to fill the chip alone
+struct FwdBatch {
+  FwdParams p[kMaxFwdBatch];
+};
+static_assert(sizeof(FwdBatch) <= 4096, "kernel arguments");
+__device__ __forceinline__ const FwdParams &fwd_pick(const FwdParams &p) { return p; }
+__device__ __forceinline__ const FwdParams &fwd_pick(const FwdBatch &b) { return b.p[blockIdx.y]; }
+
 // bf16 forward: K/V tiles arrive by asynchronous global->LDS copies into two
 // swizzled buffers, so tile t+1 is in flight while tile t is computed; one
 // barrier per tile. The loop is unrolled by two so that every LDS read names
@@ -509,8 +518,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------
 // MASK = false: launches without a causal or window mask; only the keys past
 // the end of a ragged last tile are masked.
-template <int D, typename OutT, bool MASK>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdParams p) {
+// PT: FwdParams (one forward) or FwdBatch (grid.y picks the forward)
+template <int D, typename OutT, bool MASK, typename PT>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
+  const FwdParams &p = fwd_pick(args);
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
@@ -784,11 +795,11 @@ static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid,
   if constexpr (sizeof(T) == 2) {
     const bool mask = fp.m.causal || fp.m.window > 0;
     if (out_dtype == 0) {
-      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
     } else {
-      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
     }
   } else {
     if (out_dtype == 0)
@@ -799,7 +810,7 @@ static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid,
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
+static FwdParams fwd_params(const FwdArgs &a) {
   FwdParams fp;
   fp.q = a.q.data; fp.k = a.k.data; fp.v = a.v.data;
   fp.q_st = a.q.st; fp.q_sh = a.q.sh; fp.k_st = a.k.st; fp.k_sh = a.k.sh; fp.v_st = a.v.st; fp.v_sh = a.v.sh;
@@ -814,6 +825,11 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   fp.items = a.sched.items; fp.order = a.sched.order; fp.count = a.sched.count;
   fp.acc = a.acc; fp.a_st = a.a_st; fp.a_sh = a.a_sh;
   fp.merge = a.acc != nullptr && a.merge; fp.final_view = a.final_view;
+  return fp;
+}
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
+  const FwdParams fp = fwd_params(a);
   const int64_t grid = a.grid_items * a.hq;
   if (grid <= 0) return hipSuccess;
   if (a.dtype == 0) {
@@ -822,6 +838,42 @@ hipError_t launch_fwd(const FwdArgs &a, hipStream_t s) {
   }
   if (a.head_dim == 128) return launch_fwd_t<float, 128>(fp, a.out_dtype, grid, s);
   return launch_fwd_t<float, 64>(fp, a.out_dtype, grid, s);
+}
+
+template <int D>
+static hipError_t launch_fwd_batch_t(const FwdBatch &b, bool mask, int out_dtype, int64_t grid, int n, hipStream_t s) {
+  const dim3 g((unsigned)grid, (unsigned)n);
+  if (out_dtype == 0) {
+    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdBatch>), g, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdBatch>), g, dim3(256), 0, s, b);
+  } else {
+    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdBatch>), g, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdBatch>), g, dim3(256), 0, s, b);
+  }
+  return hipGetLastError();
+}
+
+bool fwd_batchable(const FwdArgs *a, int n) {
+  if (n < 1 || n > kMaxFwdBatch || a[0].dtype != 0) return false;
+  const bool mask0 = a[0].mask.causal || a[0].mask.window > 0;
+  for (int i = 0; i < n; ++i) {
+    const bool mask = a[i].mask.causal || a[i].mask.window > 0;
+    if (a[i].dtype != 0 || a[i].head_dim != a[0].head_dim || a[i].out_dtype != a[0].out_dtype ||
+        a[i].hq != a[0].hq || a[i].grid_items != a[0].grid_items || mask != mask0)
+      return false;
+  }
+  return true;
+}
+
+hipError_t launch_fwd_batch(const FwdArgs *a, int n, hipStream_t s) {
+  if (!fwd_batchable(a, n)) return hipErrorInvalidValue;
+  FwdBatch b{};
+  for (int i = 0; i < n; ++i) b.p[i] = fwd_params(a[i]);
+  const int64_t grid = a[0].grid_items * a[0].hq;
+  if (grid <= 0) return hipSuccess;
+  const bool mask = a[0].mask.causal || a[0].mask.window > 0;
+  if (a[0].head_dim == 128) return launch_fwd_batch_t<128>(b, mask, a[0].out_dtype, grid, n, s);
+  return launch_fwd_batch_t<64>(b, mask, a[0].out_dtype, grid, n, s);
 }
 
 }  // namespace attn

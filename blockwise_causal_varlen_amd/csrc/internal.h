@@ -98,6 +98,11 @@ struct FwdArgs {
   int32_t merge = 0, final_view = 0;
 };
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t s);
+// up to kMaxFwdBatch bf16 forwards of one shape (head_dim, hq, out dtype,
+// masked or not, schedule capacity) in one launch
+constexpr int kMaxFwdBatch = 8;
+bool fwd_batchable(const FwdArgs *a, int n);
+hipError_t launch_fwd_batch(const FwdArgs *a, int n, hipStream_t s);
 
 struct DecodeArgs {
   TensorDev q, k, v;
