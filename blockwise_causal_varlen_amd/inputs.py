@@ -189,14 +189,15 @@ class KvpCase:
 
 
 def cfg4(window=0, s_q=2048, hq=8, hkv=1, d=128, num_blocks=2048, block_size=16, R=4,
-         seg_size=2048, global_q_offset=98304, seed=0):
+         seg_size=2048, global_q_offset=98304, seed=0, dtype=torch.bfloat16):
     """KV-parallel prefill: q [8, 2048, 128] bf16, 4 round-robin shards of 2048
     paged blocks of 16 tokens (random block tables), seg_size=2048,
-    global_q_offset=98304, sliding window 0 or 4096."""
+    global_q_offset=98304, sliding window 0 or 4096 (other sizes and dtypes for
+    the parity tests)."""
     g = _gen(seed)
-    q = normal((hq, s_q, d), torch.bfloat16, g)
-    kc = [normal((num_blocks, hkv, block_size, d), torch.bfloat16, g) for _ in range(R)]
-    vc = [normal((num_blocks, hkv, block_size, d), torch.bfloat16, g) for _ in range(R)]
+    q = normal((hq, s_q, d), dtype, g)
+    kc = [normal((num_blocks, hkv, block_size, d), dtype, g) for _ in range(R)]
+    vc = [normal((num_blocks, hkv, block_size, d), dtype, g) for _ in range(R)]
     tabs = [torch.randperm(num_blocks, generator=g).to(torch.int32).reshape(1, -1) for _ in range(R)]
     scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     return KvpCase(q, kc, vc, tabs, block_size, seg_size, global_q_offset, window, scale, R)

@@ -341,7 +341,7 @@ class KvpWorkload:
                            kv_interleave=case.R, block_size=case.block_size, max_blocks=self.n_blocks,
                            page_stride=self.kc[0].stride(0), seg_size=case.seg_size,
                            block_table=self.tabs[0])
-        self.out = torch.empty(s_q, hq, d, dtype=torch.bfloat16, device=device)
+        self.out = torch.empty(s_q, hq, d, dtype=case.q.dtype, device=device)
         self.lse = torch.empty(hq, s_q, dtype=torch.float32, device=device)
 
     def forward(self):

@@ -25,14 +25,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def check(out, lse, ro, rl, what):
+def check(out, lse, ro, rl, what, tol=OUT_TOL, lse_tol=LSE_TOL):
     go, gl = O.as_f64(out.cpu()), O.as_f64(lse.cpu())
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(gl), fin), f"{what}: -inf pattern of lse differs"
     e_o = float(np.max(np.abs(go - ro), initial=0.0))
     e_l = float(np.max(np.abs(gl[fin] - rl[fin]), initial=0.0))
     say(f"  {what}: out {e_o:.2e} lse {e_l:.2e}")
-    assert e_o <= OUT_TOL and e_l <= LSE_TOL, (what, e_o, e_l)
+    assert e_o <= tol and e_l <= lse_tol, (what, e_o, e_l)
 
 
 @pytest.mark.parametrize("i", range(10))
@@ -83,3 +83,19 @@ def test_random_decode(gpu_lib, i):
     torch.cuda.synchronize()
     ro, rl = O.decode_forward(case.q, case.k, case.v, case.cu_k, case.scale)
     check(out, lse, ro, rl, f"decode {i}")
+
+
+@pytest.mark.parametrize("R,dtype", [(10, torch.bfloat16), (3, torch.float32)])
+def test_kvp_rank_batches(gpu_lib, R, dtype):
+    """The ranks' forwards run batched up to 8 to a launch: 10 ranks take two
+    launches; f32 inputs take one launch per rank."""
+    say(f"kvp R={R} {dtype}")
+    case = inputs.cfg4(window=300, s_q=130, hq=4, hkv=2, d=64, num_blocks=12, block_size=16, R=R, seg_size=96,
+                       global_q_offset=R * 12 * 16 - 100, seed=9300 + R, dtype=dtype)
+    wl = W.KvpWorkload(case)
+    out, lse = wl.forward()
+    torch.cuda.synchronize()
+    ro, rl, _ = O.kvp_forward(case.q.transpose(0, 1), case.k_caches, case.v_caches, case.tables, 12, 96,
+                              R * 12 * 16 - 100, 300, case.scale, interleave=True)
+    f32 = dtype == torch.float32
+    check(out, lse, ro, rl, f"kvp R={R}", *((1e-4, 1e-5) if f32 else (OUT_TOL, LSE_TOL)))
