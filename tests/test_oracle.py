@@ -437,6 +437,84 @@ def test_kvp_merge_equals_global_attention(window, seg):
     assert np.max(np.abs(co - ro)) < 1e-12 and np.max(np.abs(cl - rl)) < 1e-12
 
 
+def test_page_table_direction_from_page():
+    """Logical block b of a rank's keys is read from physical page block_table[b]
+    (hand-worked table with a table that is not its own inverse)."""
+    f = FACTS["page_table_direction"]
+    nb, bs, d = f["num_blocks"], f["block_size"], 3
+    cache = np.zeros((nb, 2, bs, d))
+    for p in range(nb):
+        for o in range(bs):
+            cache[p, :, o, :] = 10 * p + o  # the value names (page, offset)
+    got = O.kvp_gather_pages(cache, np.array([f["block_table"]]), nb)
+    assert got.shape == (nb * bs, 2, d)
+    for c in f["logical_token_reads"]:
+        assert np.all(got[c["logical_token"]] == 10 * c["page"] + c["offset"]), c
+
+
+# --------------------------------------------------------------------------
+# block backward under the position-map and window masks
+# --------------------------------------------------------------------------
+MASKED_BWD_CASES = [
+    dict(causal=True, window=3),
+    dict(causal=True, window=4, q_pos_offset=7, k_pos_offset=2),
+    dict(causal=True, q_pos_offset=9, kv_interleave=3, kv_rank=1, block_size=2),
+    dict(causal=True, window=6, q_pos_offset=11, kv_interleave=2, kv_rank=1, block_size=3),
+    dict(q_view="back", k_view="front"),
+]
+
+
+@pytest.mark.parametrize("mask", MASKED_BWD_CASES)
+def test_block_backward_finite_differences_under_masks(mask):
+    """block_backward fed the block's own (out, lse) is the gradient of
+    L = sum(dout * out) of block_forward under the same mask; central
+    differences of L check every element of dq, dk and dv."""
+    cu_q, cu_k = [0, 5, 12], [0, 6, 14]
+    hq, hkv, d = 4, 2, 3
+    q, k, v = rnd((12, hq, d), 131), rnd((14, hkv, d), 132), rnd((14, hkv, d), 133)
+    dout = rnd((12, hq, d), 134)
+    scale = 0.55
+    out, lse = O.block_forward(q, k, v, cu_q, cu_k, scale, **mask)
+    assert np.isfinite(lse).sum() > 0
+    dq, dk, dv = O.block_backward(dout, q, k, v, out, lse, cu_q, cu_k, scale, **mask)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(dout * O.block_forward(q_, k_, v_, cu_q, cu_k, scale, **mask)[0]))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in itertools.product(*map(range, x.shape)):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            fp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            fm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(g)) > 1e-3, name  # the mask leaves gradient to check
+        err = np.max(np.abs(num - g)) / max(1.0, np.max(np.abs(g)))
+        assert err < 1e-6, (name, mask, err)
+
+
+@pytest.mark.parametrize("mask", MASKED_BWD_CASES[:4])
+def test_block_backward_key_split_sums_to_whole_under_masks(mask):
+    """With the merged (out, lse) of the whole key range, the backward of any
+    split of the keys (k_range parts) sums to the backward of the whole."""
+    cu_q, cu_k = [0, 9, 20], [0, 10, 23]
+    hq, hkv, d = 4, 1, 4
+    q, k, v = rnd((20, hq, d), 141), rnd((23, hkv, d), 142), rnd((23, hkv, d), 143)
+    dout = rnd((20, hq, d), 144)
+    out, lse = O.block_forward(q, k, v, cu_q, cu_k, 0.5, **mask)
+    whole = O.block_backward(dout, q, k, v, out, lse, cu_q, cu_k, 0.5, **mask)
+    parts = [O.block_backward(dout, q, k, v, out, lse, cu_q, cu_k, 0.5, k_range=rg, **mask)
+             for rg in ((0, 3), (3, 8), (8, 100))]
+    for i in range(3):
+        assert np.max(np.abs(sum(p[i] for p in parts) - whole[i])) < 1e-12
+
+
 # --------------------------------------------------------------------------
 # decode
 # --------------------------------------------------------------------------
