@@ -41,11 +41,40 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (AMD published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD published)
+BF16_FLOP_PER_CLK_CU = 4096  # dense bf16 MFMA flops per clock per CDNA4 compute unit
 METRIC = "causal-effective TFLOP/s fwd(+bwd) & % bf16 MFMA peak; decode GB/s & % HBM peak"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def device_peaks():
+    """The bf16 MFMA peak re-derived from the GPU agent rocminfo reports
+    (compute units x max engine clock x 4096 flop/clk/CU), beside the
+    published figures the roofline fractions use. rocminfo reports no memory
+    bandwidth, so the HBM peak is the published 8 TB/s."""
+    import re
+    import subprocess
+    info = {"bf16_tflops_published": PEAK_BF16_TFLOPS, "hbm_gbs_published": PEAK_HBM_GBS,
+            "used_for_frac": "published"}
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError) as e:
+        info["rocminfo"] = f"unavailable: {e}"
+        return info
+    for agent in txt.split("Agent ")[1:]:
+        if not re.search(r"Name:\s+gfx9", agent):
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        clk = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and clk:
+            cus, mhz = int(cu.group(1)), int(clk.group(1))
+            info.update({"rocminfo_compute_units": cus, "rocminfo_max_clock_mhz": mhz,
+                         "bf16_tflops_rocminfo": round(cus * mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12, 1)})
+            return info
+    info["rocminfo"] = "no gfx9 agent found"
+    return info
 
 
 def sources_digest():
@@ -319,8 +348,7 @@ def cpu_baseline(case, target_s, np):
     """fp64 oracle on sampled query rows of the headline workload: the 8
     forward blocks + merges and the 8 backward blocks for those rows."""
     import oracle as O
-    from threadpoolctl import threadpool_info
-    from blockwise_causal_varlen_amd import workloads as W
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     cp, r = case.cp, 3
     cu = case.cu
@@ -359,19 +387,27 @@ def cpu_baseline(case, target_s, np):
                     pairs += len(sel) * (kb - ka)
         return dt, pairs
 
-    # grow the sample until it takes about target_s (the cost per row is not
-    # linear at small samples: whole documents' keys are read per row chunk)
-    n = 16
-    dt, pairs = run(n)
-    while dt < 0.6 * target_s and n < 8192:
-        n = min(8192, int(n * min(8.0, max(1.5, 0.9 * target_s / max(dt, 1e-3)))))
+    # all the host cores this process may run on, capped by the thread count
+    # the environment grants (OMP_NUM_THREADS, when set)
+    affinity = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = min(affinity, cap) if cap > 0 else affinity
+    with threadpool_limits(limits=cores, user_api="blas"):
+        # grow the sample until it takes about target_s (the cost per row is not
+        # linear at small samples: whole documents' keys are read per row chunk)
+        n = 16
         dt, pairs = run(n)
+        while dt < 0.6 * target_s and n < 8192:
+            n = min(8192, int(n * min(8.0, max(1.5, 0.9 * target_s / max(dt, 1e-3)))))
+            dt, pairs = run(n)
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     hq, d = q.shape[1], q.shape[2]
     flops = pairs * (4 + 10) * d * hq
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "affinity_cores": affinity,
             "sample": f"{n} sampled query rows of the headline rank (fwd 8 blocks + merges, bwd 8 blocks), "
-                      f"{pairs} visible pairs x 32 heads, {dt:.1f} s on the host"}
+                      f"{pairs} visible pairs x 32 heads, {dt:.1f} s on the host, fp64 numpy with {threads} "
+                      f"BLAS threads ({affinity} cores in the affinity mask)"}
 
 
 def main():
@@ -407,6 +443,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    peaks = device_peaks()
+    log(f"peaks: {json.dumps(peaks)}")
     h = headline(args, torch, lib, I, W)
     log(f"headline: {h['ms_per_step']:.3f} ms/step, {h['value']:.1f} TFLOP/s fwd+bwd")
     case = h.pop("case")
@@ -436,6 +474,7 @@ def main():
         "roofline": {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel")},
         "cpu_baseline": cpu,
         "fraction_of_bf16_peak": round(h["value"] / PEAK_BF16_TFLOPS, 4),
+        "peaks": peaks,
         "kernels": h["kernels"],
         "kernel_ms_total": {k: {"launches": v[0], "ms": round(v[1], 4)} for k, v in h["kernel_ms"].items()},
         "rows": rows,

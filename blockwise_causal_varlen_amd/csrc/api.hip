@@ -199,7 +199,8 @@ attn_status check_qkv(const attn_tensor *q, const attn_tensor *k, const attn_ten
 }
 
 attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v, int32_t num_seqs,
-                     int32_t max_q, int32_t max_k, const attn_mask *m, Problem &P, bool allow_split = true) {
+                     int32_t max_q, int32_t max_k, const attn_mask *m, Problem &P, bool allow_split = true,
+                     bool allow_decode = true) {
   TRY(check_qkv(q, k, v));
   TRY(check_mask(m));
   if (num_seqs < 0 || max_q < 0 || max_k < 0) return fail(ATTN_ERR_CU_SEQLENS, "negative num_seqs or max_seqlen");
@@ -213,7 +214,7 @@ attn_status plan_fwd(const attn_tensor *q, const attn_tensor *k, const attn_tens
   const bool plain = !m || (!m->causal && m->q_view == 0 && m->k_view == 0 && m->window == 0 &&
                             m->kv_interleave == 0 && !m->block_table && m->seg_size == 0);
   // (the decode kernel addresses one sequence's K / V bytes with 32-bit offsets)
-  P.decode = max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16 &&
+  P.decode = allow_decode && max_q == 1 && plain && q->dtype == ATTN_BF16 && (P.hq / P.hkv) <= 16 &&
              (int64_t)max_k * (k->stride_tok > v->stride_tok ? k->stride_tok : v->stride_tok) * 2 <
                  ((int64_t)1 << 31);
   P.dsplit = 1; P.dsplit_len = 0;
@@ -358,6 +359,12 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
   return fail(ATTN_ERR_INVALID, "unknown op %d", (int)op);
 }
 
+attn_status attn_workspace_bytes(attn_op op, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
+                                 int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask,
+                                 size_t *bytes) {
+  return attn_workspace_size(op, q, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, bytes);
+}
+
 }  // extern "C"
 
 namespace {
@@ -391,7 +398,8 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
                            void *stream, const FusedMerge *fm, const SchedBufs *pre = nullptr,
                            bool allow_split = true, const PartsOut *po = nullptr, FwdArgs *defer = nullptr) {
   Problem P;
-  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm));
+  // caller-owned parts always take the tiled forward (never the decode kernel)
+  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, allow_split && !fm, po == nullptr));
   TRY(check_out(out, P, "out"));
   if (po) {
     if (P.decode || fm) return fail(ATTN_ERR_INVALID, "internal: caller-owned parts need the tiled forward");
@@ -1220,12 +1228,28 @@ static size_t kvp_gather_bytes(int32_t R, const Problem &P) {
   return (size_t)R * 2 * align256((size_t)P.n_k_logical * P.gather_row_bytes);
 }
 
+// The KV-parallel entries are always paged: the tables come in their own
+// block_tables argument, so mask->block_table is ignored and the plan is made
+// for paged keys (a host address stands in as the non-NULL table: plan_fwd
+// only tests it, nothing dereferences it).
+static const int32_t kKvpTableMarker[1] = {0};
+static attn_mask kvp_paged_mask(const attn_mask *m) {
+  attn_mask mk = *m;
+  mk.block_table = kKvpTableMarker;
+  return mk;
+}
+
 attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k, int32_t num_seqs,
-                                    int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, size_t *bytes) {
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask_in,
+                                    size_t *bytes) {
   if (!bytes) return fail(ATTN_ERR_NULL, "bytes is NULL");
   if (R < 1 || R > 16) return fail(ATTN_ERR_INVALID, "R must be in [1, 16]");
+  if (!mask_in) return fail(ATTN_ERR_NULL, "mask is NULL");
+  TRY(check_mask(mask_in));
+  const attn_mask mk = kvp_paged_mask(mask_in);
+  const attn_mask *mask = &mk;
   Problem P;
-  TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
+  TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, true, false));
   P.decode = false;
   if (kvp_all_parts(R, P) && P.gather) {
     if (P.nseg == 0) P.nseg = 1;
@@ -1241,12 +1265,14 @@ attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_
 
 attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_caches, const attn_tensor *v_caches,
                          const int32_t *const *block_tables, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
-                         int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask,
+                         int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask_in,
                          float scale, const attn_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
                          void *stream) {
   if (R < 1 || R > 16) return fail(ATTN_ERR_INVALID, "R must be in [1, 16]");
-  if (!k_caches || !v_caches || !block_tables || !mask) return fail(ATTN_ERR_NULL, "NULL argument");
-  TRY(check_mask(mask));
+  if (!k_caches || !v_caches || !block_tables || !mask_in) return fail(ATTN_ERR_NULL, "NULL argument");
+  TRY(check_mask(mask_in));
+  const attn_mask mk = kvp_paged_mask(mask_in);
+  const attn_mask *mask = &mk;
   if (mask->kv_interleave != 0 && mask->kv_interleave != R)
     return fail(ATTN_ERR_INVALID, "kv_interleave must be 0 (contiguous) or R");
   size_t need = 0;
@@ -1256,8 +1282,7 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
   if (!lse && q->n_tok > 0) return fail(ATTN_ERR_NULL, "lse is NULL");
   char *w = (char *)workspace;
   Problem P;
-  TRY(plan_fwd(q, &k_caches[0], &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, P));
-  P.decode = false;
+  TRY(plan_fwd(q, &k_caches[0], &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, P, true, false));
   if (kvp_all_parts(R, P) && P.gather) {
     const int64_t n = P.nseg > 0 ? P.nseg : 1;
     const int64_t slice = P.n_q * P.hq * P.d, lslice = P.hq * P.n_q;

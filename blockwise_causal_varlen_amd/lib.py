@@ -63,6 +63,7 @@ _SIGS = {
     "attn_status_string": (C.c_char_p, [C.c_int]),
     "attn_last_error": (C.c_char_p, []),
     "attn_workspace_size": (C.c_int, [C.c_int, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
+    "attn_workspace_bytes": (C.c_int, [C.c_int, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
     "attn_block_fwd": (C.c_int, [T, T, T, P, P, I32, I32, I32, M, F, T, P, P, SZ, P]),
     "attn_merge_out_lse": (C.c_int, [T, P, T, P, P, I32, U32, P, T, I32, P]),
     "attn_merge_n": (C.c_int, [I32, T, C.POINTER(P), T, P, P]),

@@ -160,6 +160,11 @@ const char *attn_last_error(void);
 attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_tensor *k,
                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                 const attn_mask *mask, size_t *bytes);
+/* attn_workspace_bytes -- the same query under a second name (identical
+ * arguments, result and errors as attn_workspace_size). */
+attn_status attn_workspace_bytes(attn_op op, const attn_tensor *q, const attn_tensor *k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const attn_mask *mask, size_t *bytes);
 
 /*
  * attn_block_fwd -- one attention block -> (out, lse).
@@ -454,6 +459,12 @@ attn_status attn_ring_bwd_ex(int32_t cp, int32_t rank, const attn_tensor *dout,
  *   k_caches, v_caches  host arrays of R cache descriptors
  *   block_tables        host array of R device pointers (each max_blocks int32)
  *   cu_seqlens_k        logical local key counts per document
+ *   mask                required; block_size, max_blocks and page_stride must
+ *                       be > 0 (ATTN_ERR_INVALID otherwise). The keys are
+ *                       always paged through block_tables: mask->block_table
+ *                       is ignored by both entries. The per-rank forwards are
+ *                       always tiled (max_seqlen_q == 1 does not select the
+ *                       decode kernel here).
  * 1 <= R <= 16. Workspace: attn_kvp_workspace_size bytes.
  */
 attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_tensor *k,

@@ -677,12 +677,13 @@ def kvp_rank_partial(q, k_cache, v_cache, block_table, n_blocks, R, r, seg_size,
 
 
 def kvp_forward(q, k_caches, v_caches, tables, n_blocks, seg_size, global_q_offset, window, scale,
-                interleave=True, rows=None):
+                interleave=True, rows=None, causal=True):
     """[KVP] merged output: the R ranks' partials merged by online softmax
     (rank order 0..R-1). Returns (out, lse, partials). q is [S, HQ, D]."""
     R = len(k_caches)
     parts = [kvp_rank_partial(q, k_caches[r], v_caches[r], tables[r], n_blocks, R, r, seg_size,
-                              global_q_offset, window, scale, interleave, rows=rows) for r in range(R)]
+                              global_q_offset, window, scale, interleave, causal=causal, rows=rows)
+             for r in range(R)]
     out, lse = parts[0]
     for r in range(1, R):
         out, lse, _ = merge(out, lse, *parts[r])

@@ -99,6 +99,34 @@ def test_workspace_size_is_host_only(so):
     assert L.attn_workspace_size(L.OP_BLOCK_BWD, q, k, 3, 500, 500, None) > 0
 
 
+def test_workspace_bytes_alias_and_kvp_paging(so):
+    """attn_workspace_bytes answers as attn_workspace_size; the KV-parallel
+    workspace is planned for paged keys whether or not the mask carries a
+    block_table (the tables come in their own argument), and a mask without
+    page sizes is refused."""
+    lib = L.load()
+    q, k = T(n=1000, h=8), T(n=1000, h=2)
+    for m in (L.mask(causal=True), L.mask(causal=True, seg_size=128), None):
+        a, b = C.c_size_t(0), C.c_size_t(0)
+        ref = None if m is None else C.byref(m)
+        assert lib.attn_workspace_size(0, C.byref(q), C.byref(k), 3, 500, 500, ref, C.byref(a)) == 0
+        assert lib.attn_workspace_bytes(0, C.byref(q), C.byref(k), 3, 500, 500, ref, C.byref(b)) == 0
+        assert a.value == b.value > 0
+    assert lib.attn_workspace_bytes(5, C.byref(q), C.byref(k), 3, 500, 500, None, C.byref(a)) == 11
+    qk, kc = T(n=1, h=4), T(n=320, h=2)
+    sizes = []
+    for bt in (None, torch.zeros(20, dtype=torch.int32)):
+        m = L.mask(block_size=16, max_blocks=20, page_stride=2 * 16 * 128, block_table=bt)
+        n = C.c_size_t(0)
+        assert lib.attn_kvp_workspace_size(3, C.byref(qk), C.byref(kc), 1, 1, 320, C.byref(m), C.byref(n)) == 0
+        sizes.append(n.value)
+    assert sizes[0] == sizes[1] >= 3 * 2 * 320 * 2 * 128 * 2      # the three ranks' gathered K and V
+    n = C.c_size_t(0)
+    m = L.mask(causal=True)
+    assert lib.attn_kvp_workspace_size(3, C.byref(qk), C.byref(kc), 1, 1, 320, C.byref(m), C.byref(n)) == 11
+    assert lib.attn_kvp_workspace_size(3, C.byref(qk), C.byref(kc), 1, 1, 320, None, C.byref(n)) == 1
+
+
 def test_merge_and_bwd_error_codes(so):
     lib = L.load()
     o = T(dtype=L.F32)

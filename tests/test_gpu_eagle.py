@@ -63,10 +63,8 @@ def test_eagle_zigzag_all_ranks(gpu_lib, which):
         say(f" rank {r}")
         check("out", wl.final[r].cpu(), shard(ro, cu, cp, r))
         check("lse", run.lse.cpu(), shard(rl.T, cu, cp, r).T, LSE_TOL)
-    # backward at the GPU's merged state
-    gout = O.zigzag_unshard([f64(wl.final[r].cpu()) for r in range(cp)], cu, cp)
-    glse = O.zigzag_unshard([f64(wl.zz.runners[r].lse.cpu()).T for r in range(cp)], cu, cp).T
-    dq, dks, dvs = O.eagle_grads(base.dout, base.q, ks, vs, cu, base.scale, out=gout, lse=glse)
+    # end to end: the oracle's gradients of its own joint softmax
+    dq, dks, dvs = O.eagle_grads(base.dout, base.q, ks, vs, cu, base.scale)
     dk0 = [torch.zeros_like(wl.zz.runners[0].dk[s]) for s in range(cp)]
     dv0 = [torch.zeros_like(wl.zz.runners[0].dv[s]) for s in range(cp)]
     for r in range(cp):

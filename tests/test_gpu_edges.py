@@ -121,12 +121,15 @@ def test_rows_that_see_nothing(gpu_lib, mname):
 
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 1)])
 def test_mha_and_wide_gqa(gpu_lib, hq, hkv):
-    """MHA (one q head per kv head) and 16 q heads sharing one kv head. dK and
-    dV sum over the group's heads, so with 16 heads their magnitude (max |dV|
-    ~16 here) outgrows the absolute 2e-2 bar set for the 4-way benchmark
-    shapes: the products take P and dS rounded to bf16 (relative 2^-9), so the
-    bar for the gradients is max(2e-2, 2^-9 max|ref|) (measured 1.4e-3 of
-    max|dV| on this case)."""
+    """MHA (one q head per kv head) and 16 q heads sharing one kv head.
+
+    OUTSIDE THE STATED BOUND: this is the one test whose gradients are not
+    held to the absolute 2e-2 bar. dK and dV sum over the group's heads, so
+    with 16 heads their magnitude (max |dV| ~16 here) outgrows a bar set for
+    gradients of order <= 10 (the benchmark shapes have at most 4 q heads per
+    kv head): the products take P and dS rounded to bf16 (relative 2^-9), so
+    the gradients here are held to max(2e-2, 2^-9 max|ref|) (measured 2.3e-2
+    absolute, 1.4e-3 of max|dV|). Forward out and lse keep the stated bars."""
     L = gpu_lib
     lens = [200, 77, 129]
     cu_q, cu_k, q, k, v, dout = case(lens, lens, hq, hkv, 128, seed=4)

@@ -7,6 +7,7 @@ combination of causal, sliding window, position offsets, round-robin key
 positions and half views. The forward (out, lse) and the backward (dq, dk, dv,
 with the block's own out and lse as the merged state) are checked element by
 element; rows outside the query view must keep what the caller left there.
+Gradients are held to the absolute bar (2e-2 for bf16, 1e-4 for f32).
 """
 
 import math
@@ -108,4 +109,4 @@ def test_random_block(gpu_lib, i):
         e = float(np.max(np.abs(O.as_f64(gt.cpu()) - r), initial=0.0))
         big = float(np.max(np.abs(r), initial=0.0))
         say(f"  {name}: {e:.2e} (max |ref| {big:.2f})")
-        assert e <= max(tol, (2.0 ** -9 if dtype == torch.bfloat16 else 0.0) * big), (name, e)
+        assert e <= tol, (name, e)

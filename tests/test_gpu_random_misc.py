@@ -99,3 +99,20 @@ def test_kvp_rank_batches(gpu_lib, R, dtype):
                               R * 12 * 16 - 100, 300, case.scale, interleave=True)
     f32 = dtype == torch.float32
     check(out, lse, ro, rl, f"kvp R={R}", *((1e-4, 1e-5) if f32 else (OUT_TOL, LSE_TOL)))
+
+
+def test_kvp_one_query_unmasked_contiguous(gpu_lib):
+    """A single query row, no causal mask, no window, contiguous shards and no
+    block_table in the mask: the driver pages through block_tables and runs
+    the tiled forward for every rank (not the one-query decode kernel)."""
+    case = inputs.cfg4(window=0, s_q=1, hq=4, hkv=2, d=128, num_blocks=20, block_size=16, R=3, seg_size=0,
+                       global_q_offset=700, seed=9400)
+    wl = W.KvpWorkload(case)
+    wl.mask.causal = 0
+    wl.mask.kv_interleave = 0
+    wl.mask.block_table = None
+    out, lse = wl.forward()
+    torch.cuda.synchronize()
+    ro, rl, _ = O.kvp_forward(case.q.transpose(0, 1), case.k_caches, case.v_caches, case.tables, 20, 0, 700, 0,
+                              case.scale, interleave=False, causal=False)
+    check(out, lse, ro, rl, "kvp one query")

@@ -85,9 +85,8 @@ def test_zigzag_forward_backward_all_ranks(gpu_lib, which):
         say(f" rank {r}")
         check("out", run.out.cpu(), ro, OUT_TOL)
         check_lse("lse", run.lse.cpu(), rl)
-        # backward of the GPU's merged state (its out in q dtype and its lse)
-        dq, dk, dv = O.zigzag_backward(odo[r], oqs, oks, ovs, f64(run.out.cpu()), f64(run.lse.cpu()), cu, cp, r,
-                                       case.scale)
+        # end to end: the oracle's backward at the oracle's own merged state
+        dq, dk, dv = O.zigzag_backward(odo[r], oqs, oks, ovs, ro, rl, cu, cp, r, case.scale)
         check("dq", run.dq.cpu(), dq, OUT_TOL)
         for s in range(cp):
             dk_sum[s] += dk[s]
@@ -150,23 +149,50 @@ def test_zigzag_cfg3_one_rank_sampled(gpu_lib):
         ro, lo = (bo, bl) if ro is None else O.merge(ro, lo, bo, bl)[:2]
     check("out (sampled rows)", run.out.cpu()[rows], ro[rows], OUT_TOL)
     check_lse("lse (sampled rows)", run.lse.cpu()[:, rows], lo[:, rows])
-    # backward on the GPU's merged state
-    out_m, lse_m = f64(run.out.cpu()), f64(run.lse.cpu())
+    # end to end: dq on the sampled rows, the oracle's backward at its own merged state
     dq = np.zeros((len(rows),) + tuple(qloc.shape[1:]))
+    for s in range(cp):
+        src, kind = O.zigzag_step(r, s, cp)
+        gq, _, _ = O.block_backward(dout, qloc, oks[src], ovs[src], ro, lo, cu_l, cu_l, case.scale,
+                                    rows=rows, **O.zigzag_block_args(kind))
+        dq += gq[rows]
+    check("dq (sampled rows, oracle state)", run.dq.cpu()[rows], dq, OUT_TOL)
+    # end to end: dk/dv of every owner on sampled key rows of the two shortest
+    # documents, at the oracle's merged state of every row of those documents
+    lens_l = cu_l[1:] - cu_l[:-1]
+    docs = np.argsort(lens_l, kind="stable")[:2]
+    drows = np.concatenate([np.arange(cu_l[d], cu_l[d + 1]) for d in docs])
+    eo = el = None
+    for s in range(cp):
+        src, kind = O.zigzag_step(r, s, cp)
+        bo, bl = O.block_forward(qloc, oks[src], ovs[src], cu_l, cu_l, case.scale, rows=drows,
+                                 **O.zigzag_block_args(kind))
+        eo, el = (bo, bl) if eo is None else O.merge(eo, el, bo, bl)[:2]
+    rng = np.random.default_rng(2)
+    ke = set(rng.choice(drows, size=min(24, len(drows)), replace=False).tolist())
+    for d in docs:
+        a0, b0 = int(cu_l[d]), int(cu_l[d + 1])
+        ke.update([a0, b0 - 1, (a0 + b0) // 2, (a0 + b0) // 2 - 1])
+    ke = np.array(sorted(ke))
+    say(f" {len(ke)} sampled key rows of documents {docs.tolist()} (end to end)")
+    for s in range(cp):
+        src, kind = O.zigzag_step(r, s, cp)
+        _, gk, gv = O.block_backward(dout, qloc, oks[src], ovs[src], eo, el, cu_l, cu_l, case.scale,
+                                     krows=ke, **O.zigzag_block_args(kind))
+        check(f"dk owner {src} (sampled, oracle state)", run.dk[src].cpu()[ke], gk[ke], OUT_TOL)
+        check(f"dv owner {src} (sampled, oracle state)", run.dv[src].cpu()[ke], gv[ke], OUT_TOL)
+    # the block backward as a function of its merged input: the GPU's state,
+    # key rows sampled over every document
+    out_m, lse_m = f64(run.out.cpu()), f64(run.lse.cpu())
     krows = _sample_rows(case.q.shape[0], cu_l, 48, seed=1)
     dks = [np.zeros((len(krows), 8, 128)) for _ in range(cp)]
     dvs = [np.zeros((len(krows), 8, 128)) for _ in range(cp)]
     for s in range(cp):
         src, kind = O.zigzag_step(r, s, cp)
-        a = O.zigzag_block_args(kind)
-        gq, _, _ = O.block_backward(dout, qloc, oks[src], ovs[src], out_m, lse_m, cu_l, cu_l, case.scale,
-                                    rows=rows, **a)
-        dq += gq[rows]
         _, gk, gv = O.block_backward(dout, qloc, oks[src], ovs[src], out_m, lse_m, cu_l, cu_l, case.scale,
-                                     krows=krows, **a)
+                                     krows=krows, **O.zigzag_block_args(kind))
         dks[src] += gk[krows]
         dvs[src] += gv[krows]
-    check("dq (sampled rows)", run.dq.cpu()[rows], dq, OUT_TOL)
     for s in range(cp):
         check(f"dk owner {s} (sampled)", run.dk[s].cpu()[krows], dks[s], OUT_TOL)
         check(f"dv owner {s} (sampled)", run.dv[s].cpu()[krows], dvs[s], OUT_TOL)
@@ -197,8 +223,7 @@ def test_ring_forward_backward(gpu_lib):
         say(f" ring rank {r}")
         check("out", run.out.cpu(), ro, OUT_TOL)
         check_lse("lse", run.lse.cpu(), rl)
-        dq, dk, _ = O.ring_backward(odo[r], oq, ok, ov, f64(run.out.cpu()), f64(run.lse.cpu()), cu, cp, r,
-                                    1 / math.sqrt(d))
+        dq, dk, _ = O.ring_backward(odo[r], oq, ok, ov, ro, rl, cu, cp, r, 1 / math.sqrt(d))
         check("dq", run.dq.cpu(), dq, OUT_TOL)
         for s in range(cp):
             gdk[s] += f64(run.dk[s].cpu())
