@@ -297,12 +297,41 @@ size_t fwd_ws_bytes(const Problem &P, int32_t num_seqs, bool own_parts = true) {
   return b;
 }
 
-size_t bwd_ws_bytes(int64_t n_q, int64_t n_k, int64_t hq, int32_t num_seqs, bool need_delta) {
+// f16 copies of q and dout for the dK/dV kernel (bf16 inputs) and their flag
+size_t half_copy_bytes(int64_t n_q, int64_t hq, int64_t d, int32_t dtype) {
+  return dtype == ATTN_BF16 ? 2 * align256((size_t)n_q * hq * d * 2) + 256 : 0;
+}
+
+size_t bwd_ws_bytes(int64_t n_q, int64_t n_k, int64_t hq, int64_t d, int32_t dtype, int32_t num_seqs,
+                    bool need_delta) {
   size_t b = align256(sched_bytes(sched_capacity(n_q, num_seqs, kBwdTile, 1)));
   b += align256(sched_bytes(sched_capacity(n_k, num_seqs, kBwdTile, 1)));
   b += align256((size_t)hq * n_q * 4);  // lse in log2 units
   if (need_delta) b += align256((size_t)hq * n_q * 4);
-  return b;
+  return b + half_copy_bytes(n_q, hq, d, dtype);
+}
+
+// Carve the f16 copies (q16, do16, flag) at w; their launch follows lse2's,
+// which zeroes the flag.
+struct HalfCopies {
+  void *q16 = nullptr, *do16 = nullptr;
+  int32_t *flag = nullptr;
+};
+HalfCopies half_carve(char *w, int64_t n_q, int64_t hq, int64_t d) {
+  HalfCopies h;
+  const size_t b = align256((size_t)n_q * hq * d * 2);
+  h.q16 = w;
+  h.do16 = w + b;
+  h.flag = (int32_t *)(w + 2 * b);
+  return h;
+}
+hipError_t launch_half_copies(const HalfCopies &h, const attn_tensor *q, const attn_tensor *dout, hipStream_t s) {
+  HalfCopyArgs a;
+  a.q = q->data; a.q_st = q->stride_tok; a.q_sh = q->stride_head;
+  a.dout = dout->data; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
+  a.q16 = h.q16; a.do16 = h.do16; a.flag = h.flag;
+  a.n = q->n_tok; a.h = (int32_t)q->n_head; a.d = (int32_t)q->head_dim;
+  return launch_half_copy(a, s);
 }
 
 attn_status check_out(const attn_tensor *out, const Problem &P, const char *name) {
@@ -353,7 +382,7 @@ attn_status attn_workspace_size(attn_op op, const attn_tensor *q, const attn_ten
     return ok();
   }
   if (op == ATTN_OP_BLOCK_BWD) {
-    *bytes = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, true);
+    *bytes = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, q->head_dim, q->dtype, num_seqs, true);
     return ok();
   }
   return fail(ATTN_ERR_INVALID, "unknown op %d", (int)op);
@@ -754,6 +783,7 @@ namespace {
 struct BwdPre {
   SchedBufs sq, sk;
   const float *lse2;
+  HalfCopies h16;
 };
 
 attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
@@ -797,7 +827,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
   if (pre) {
     if (!delta) return fail(ATTN_ERR_INVALID, "internal: precomputed schedules need delta");
   } else {
-    const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, num_seqs, delta == nullptr);
+    const size_t need = bwd_ws_bytes(q->n_tok, k->n_tok, q->n_head, q->head_dim, q->dtype, num_seqs, delta == nullptr);
     if (!workspace || workspace_bytes < need)
       return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
     if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -808,10 +838,11 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
   MaskDev md = mask_dev(mask);
   SchedBufs sq, sk;
   const float *lse2;
+  HalfCopies h16;
   if (pre) {
     if (pre->sq.capacity != capq || pre->sk.capacity != capk)
       return fail(ATTN_ERR_INVALID, "internal: schedule capacity differs");
-    sq = pre->sq; sk = pre->sk; lse2 = pre->lse2;
+    sq = pre->sq; sk = pre->sk; lse2 = pre->lse2; h16 = pre->h16;
   } else {
     char *w = (char *)workspace;
     sq = sched_carve(w, capq);
@@ -820,13 +851,18 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
     w += align256(sched_bytes(capk));
     float *l2 = (float *)w;
     w += align256((size_t)q->n_head * q->n_tok * 4);
-    TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, l2, q->n_head * q->n_tok, s); }), "lse2"));
-    lse2 = l2;
     if (!delta) {
       float *dl = (float *)w;
+      w += align256((size_t)q->n_head * q->n_tok * 4);
       TRY(attn_bwd_delta(dout, out, dl, stream));
       delta = dl;
     }
+    if (q->dtype == ATTN_BF16) h16 = half_carve(w, q->n_tok, q->n_head, q->head_dim);
+    TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, l2, q->n_head * q->n_tok, s, h16.flag); }),
+                  "lse2"));
+    lse2 = l2;
+    if (h16.q16)
+      TRY(hip_check(timed("attn_half_copy", s, [&] { return launch_half_copies(h16, q, dout, s); }), "f16 copies"));
     const SchedJob jobs[2] = {
         {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN, 0, 1, sq},
         {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ, 1, 1, sk}};
@@ -841,6 +877,7 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
   a.dv = (float *)dv->data; a.dv_st = dv->stride_tok; a.dv_sh = dv->stride_head;
   a.qsched = sq; a.ksched = sk; a.q_items = capq; a.k_items = capk;
   a.set_q = set_q; a.set_kv = set_kv;
+  a.q16 = h16.q16; a.do16 = h16.do16; a.h16_flag = h16.flag;
   TRY(hip_check(timed("attn_dkdv", s, [&] { return launch_bwd(a, 0, s); }), "dK/dV kernel"));
   return hip_check(timed("attn_dq", s, [&] { return launch_bwd(a, 1, s); }), "dQ kernel");
 }
@@ -909,7 +946,7 @@ constexpr int kRingKinds = 3;
 
 struct RingLayout {
   size_t bout_off, blse_off, fwd_off, fsched_off, total;  // forward
-  size_t delta_off, lse2_off, bsched_off, btotal;           // backward
+  size_t delta_off, lse2_off, bsched_off, h16_off, btotal;  // backward
   int64_t fcap, qcap, kcap;
   size_t fsched_stride, bsched_stride;
 };
@@ -932,7 +969,8 @@ RingLayout ring_layout(const attn_tensor *q, const attn_tensor *k, int32_t num_s
   L.delta_off = 0;
   L.lse2_off = align256((size_t)q->n_head * q->n_tok * 4);
   L.bsched_off = 2 * L.lse2_off;
-  L.btotal = L.bsched_off + kRingKinds * L.bsched_stride;
+  L.h16_off = L.bsched_off + kRingKinds * L.bsched_stride;
+  L.btotal = L.h16_off + half_copy_bytes(q->n_tok, q->n_head, q->head_dim, q->dtype);
   return L;
 }
 
@@ -1113,7 +1151,13 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
   TRY(attn_bwd_delta(dout, out, delta, stream));
   std::vector<BwdPre> pre(kinds.size());
   if (num_seqs > 0 && q->n_tok > 0) {
-    TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st); }), "lse2"));
+    HalfCopies h16;
+    if (q->dtype == ATTN_BF16) h16 = half_carve(w + L.h16_off, q->n_tok, q->n_head, q->head_dim);
+    TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st, h16.flag); }),
+                  "lse2"));
+    if (h16.q16)
+      TRY(hip_check(timed("attn_half_copy", st, [&] { return launch_half_copies(h16, q, dout, st); }), "f16 copies"));
+    for (auto &pr : pre) pr.h16 = h16;
     SchedJob jobs[2 * kRingKinds];
     for (size_t i = 0; i < kinds.size(); ++i) {
       char *b = w + L.bsched_off + i * L.bsched_stride;

@@ -47,6 +47,10 @@ struct BwdParams {
   float *dv; int64_t dv_st, dv_sh;
   const WorkItem *items; const int32_t *order; const int32_t *count;
   int32_t set_q, set_kv;  // store dq / dk, dv instead of adding to them
+  // half-precision copies of q and dout ([n_q, HQ, D] contiguous) for the
+  // dK/dV kernel, and their flag (nonzero: a value did not fit f16); NULL: none
+  const void *q16, *do16;
+  const int32_t *h16_flag;
 };
 
 // Row-operand fragment of a 32x32 MFMA from a tile in LDS: lane row `r`, k-step s.
@@ -400,32 +404,65 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
 // through buffer resources; rows past the end of a tile read as zeros, which
 // contribute nothing: zero q/dout rows give dS = 0 and P^T dout = 0).
 // ---------------------------------------------------------------------------
-__global__ void lse2_kernel(const float *lse, float *lse2, int64_t n) {
+__global__ void lse2_kernel(const float *lse, float *lse2, int64_t n, int32_t *h16_flag) {
+  if (h16_flag && blockIdx.x == 0 && threadIdx.x == 0) *h16_flag = 0;  // before half_copy_kernel sets it
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const float l = lse[i];
     lse2[i] = l == neg_inf() ? __builtin_inff() : l * kLog2e;
   }
 }
 
+// Half-precision copies of q and dout for the dK/dV kernel: every bf16 value
+// converts to f16 exactly when |x| <= 65504 (f16 keeps 11 significant bits to
+// bf16's 8; below 2^-14 the copy is subnormal, off by at most 2^-25). A value
+// beyond that range sets *flag, and the dK/dV kernel then keeps bf16.
+// Grid-stride over 8-element pieces; q and dout have the same [n, H, D] shape.
+__global__ __launch_bounds__(256) void half_copy_kernel(const bf16 *q, int64_t q_st, int64_t q_sh, const bf16 *dout,
+                                                        int64_t do_st, int64_t do_sh, f16 *q16, f16 *do16, int64_t n,
+                                                        int32_t h, int32_t d, int32_t *flag) {
+  const int32_t per_row = h * (d / 8);
+  const int64_t total = n * per_row;
+  bool bad = false;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / per_row;
+    const int32_t r = (int32_t)(i - row * per_row), hh = r / (d / 8), c = (r - hh * (d / 8)) * 8;
+    const int64_t o16 = (row * h + hh) * d + c;
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(q + row * q_st + hh * q_sh + c));
+    const bf16x8 b = __builtin_bit_cast(bf16x8, ld16(dout + row * do_st + hh * do_sh + c));
+    f16x8 qa, ob;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (float)a[e], y = (float)b[e];
+      bad |= !(fabsf(x) <= 65504.f) | !(fabsf(y) <= 65504.f);
+      qa[e] = (f16)x;
+      ob[e] = (f16)y;
+    }
+    st16(q16 + o16, __builtin_bit_cast(i32x4, qa));
+    st16(do16 + o16, __builtin_bit_cast(i32x4, ob));
+  }
+  if (bad) *flag = 1;
+}
+
 // MASK = false: launches without a causal or window mask (every visible tile is
 // full), whose softmax step then carries no select.
-template <int D, bool MASK>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdParams p) {
-  using M = Mfma32<bf16>;
+// E: the element type of the MFMA operands. f16 (q, dout from their f16
+// copies, k and v converted in registers; P and dS rounded to f16) unless a
+// value does not fit f16, then bf16 (the inputs as given; P and dS rounded to
+// bf16). Returns false, having done nothing, when E = f16 and this
+// workgroup's k or v does not fit f16.
+template <int D, bool MASK, typename E>
+__device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *sQ1, E *sO1, float *sL0, float *sD0,
+                                         float *sL1, float *sD1) {
+  using M = Mfma32<E>;
+  using Frag = typename M::Frag;
+  typedef E E4 __attribute__((ext_vector_type(4)));
+  constexpr bool kHalf = sizeof(E) == 2 && !std::is_same<E, bf16>::value;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
   constexpr int QB = kBwdBQ;
   static_assert(QB == 64, "tiles are 64 rows");
   // row reads and transpose reads: swizzled (D = 128) or padded (at most 2-way)
   using QT = std::conditional_t<D == 128, SwzTile128, PadTile<D, D / 8 + 5>>;
-  __shared__ __attribute__((aligned(1024))) bf16 sQ0[QT::ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 sO0[QT::ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 sQ1[QT::ELEMS];
-  __shared__ __attribute__((aligned(1024))) bf16 sO1[QT::ELEMS];
-  __shared__ __attribute__((aligned(16))) float sL0[QB];
-  __shared__ __attribute__((aligned(16))) float sD0[QB];
-  __shared__ __attribute__((aligned(16))) float sL1[QB];
-  __shared__ __attribute__((aligned(16))) float sD1[QB];
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,7 +473,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   const int cap = gridDim.x / hkv_count;
   const int rank = lb % cap;
   const int hk = lb / cap;
-  if (rank >= *p.count) return;
   const WorkItem it = p.items[p.order[rank]];
   // every position and index fits in 32 bits (checked on the host)
   const int32_t q0 = it.q0, q1 = it.q1, qd0 = it.qdoc0, k1 = it.k1, kd0 = it.kdoc0;
@@ -460,34 +496,53 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   const int32_t wk_lo = kpos(kr0 - kd0);
   const int32_t wk_hi = kpos((kr0 + 31 < k1 ? kr0 + 31 : k1 - 1) - kd0);
 
-  bf16x8 kf[NS], vf[NS];
+  Frag kf[NS], vf[NS];
   {
     const bf16 *krow = (const bf16 *)p.k + (int64_t)key * p.k_st + (int64_t)hk * p.k_sh;
     const bf16 *vrow = (const bf16 *)p.v + (int64_t)key * p.v_st + (int64_t)hk * p.v_sh;
+    bool bad = false;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      kf[s] = glob_row_frag<bf16>(krow, s, g, key_ok);
-      vf[s] = glob_row_frag<bf16>(vrow, s, g, key_ok);
+      const bf16x8 kb = glob_row_frag<bf16>(krow, s, g, key_ok);
+      const bf16x8 vb = glob_row_frag<bf16>(vrow, s, g, key_ok);
+      if constexpr (kHalf) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)kb[e], y = (float)vb[e];
+          bad |= !(fabsf(x) <= 65504.f) | !(fabsf(y) <= 65504.f);
+          kf[s][e] = (f16)x;
+          vf[s][e] = (f16)y;
+        }
+      } else {
+        kf[s] = kb;
+        vf[s] = vb;
+      }
     }
+    // every wave of the workgroup takes the same path
+    if constexpr (kHalf)
+      if (__syncthreads_or(bad)) return false;
   }
   f32x16 dk[ND], dv[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
 
+  // the q / dout rows: the f16 copies ([n_q, HQ, D] contiguous) or the inputs
+  const int64_t q_st = kHalf ? (int64_t)p.hq * D : p.q_st, q_sh = kHalf ? (int64_t)D : p.q_sh;
+  const int64_t do_st = kHalf ? (int64_t)p.hq * D : p.do_st, do_sh = kHalf ? (int64_t)D : p.do_sh;
   int qoffs[QT::NJ], ooffs[QT::NJ];
-  tile_voffsets<QT>(qoffs, p.q_st, w, lane);
-  tile_voffsets<QT>(ooffs, p.do_st, w, lane);
+  tile_voffsets<QT>(qoffs, q_st, w, lane);
+  tile_voffsets<QT>(ooffs, do_st, w, lane);
   int ro[NS], trl[ND], trh[ND];  // swizzled tiles: per-lane read offsets
   if constexpr (QT::kSwz) {
     swz_row_offsets<NS>(ro, lane);
     swz_tr_offsets<ND>(trl, trh, lane);
   }
-  const int32_t qst = (int32_t)p.q_st, ost = (int32_t)p.do_st;
+  const int32_t qst = (int32_t)q_st, ost = (int32_t)do_st;
   const int32_t nqt = (q1 - q0 + QB - 1) / QB;
   const int32_t total = p.group * nqt;
   const int32_t h0 = hk * p.group;
-  const bf16 *qb = (const bf16 *)p.q;
-  const bf16 *ob = (const bf16 *)p.dout;
+  const bf16 *qb = (const bf16 *)(kHalf ? p.q16 : p.q);
+  const bf16 *ob = (const bf16 *)(kHalf ? p.do16 : p.dout);
 
   // (q head, tile start) of the next tile to stage and of the next to compute
   int32_t sh = h0, sqt = q0, ch = h0, cqt = q0;
@@ -496,10 +551,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     if (qt >= q1) { qt = q0; ++h; }
   };
 
-  auto stage = [&](bf16 *sq, bf16 *so, float *sl, float *sd) {
+  auto stage = [&](E *sq, E *so, float *sl, float *sd) {
     const int32_t nvalid = q1 - sqt < QB ? q1 - sqt : QB;
-    dma_tile_buf<QT>(sq, qb + (int64_t)sqt * p.q_st + (int64_t)sh * p.q_sh, ((nvalid - 1) * qst + D) * 2, qoffs, w);
-    dma_tile_buf<QT>(so, ob + (int64_t)sqt * p.do_st + (int64_t)sh * p.do_sh, ((nvalid - 1) * ost + D) * 2, ooffs, w);
+    dma_tile_buf<QT>((bf16 *)sq, qb + (int64_t)sqt * q_st + (int64_t)sh * q_sh, ((nvalid - 1) * qst + D) * 2, qoffs,
+                     w);
+    dma_tile_buf<QT>((bf16 *)so, ob + (int64_t)sqt * do_st + (int64_t)sh * do_sh, ((nvalid - 1) * ost + D) * 2,
+                     ooffs, w);
     if (w < 2) {
       const float *src = (w == 0 ? p.lse2 : p.delta) + (int64_t)sh * p.n_q + sqt;
       const auto rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, nvalid * 4, kBufFlags);
@@ -509,17 +566,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   };
 
   // A operand: rows sub*32 + l32 of a Q / dO tile, k-step st (d columns)
-  auto afrag = [&](const bf16 *t, int sub, int st) -> bf16x8 {
+  auto afrag = [&](const E *t, int sub, int st) -> Frag {
     const int off = QT::kSwz ? sub * 32 * 128 + ro[st] : (sub * 32 + l32) * QT::PITCH + st * 16 + g * 8;
-    return *reinterpret_cast<const bf16x8 *>(t + off);
+    return *reinterpret_cast<const Frag *>(t + off);
   };
   // transposed A operand: d rows dt*32.. of a tile, k = its rows r0 + 16 tt +
   // c_row order (the lane's rows 4g + u/4 and 8 more)
   const int u = lane & 15, dh = (lane >> 4) & 1;
-  auto trfrag = [&](const bf16 *t, int r0, int tt, int dt) -> bf16x8 {
-    const bf16 *lo_p, *hi_p;
+  auto trfrag = [&](const E *t, int r0, int tt, int dt) -> Frag {
+    const E *lo_p, *hi_p;
     if constexpr (QT::kSwz) {
-      const bf16 *blk = t + (r0 + tt * 16) * 128;
+      const E *blk = t + (r0 + tt * 16) * 128;
       lo_p = blk + trl[dt];
       hi_p = blk + trh[dt];
     } else {
@@ -528,9 +585,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
       lo_p = t + ra * QT::PITCH + col;
       hi_p = t + (ra + 8) * QT::PITCH + col;
     }
-    const bf16x4 l4 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo_p));
-    const bf16x4 h4 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi_p));
-    bf16x8 r;
+    const E4 l4 = __builtin_bit_cast(E4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)lo_p));
+    const E4 h4 = __builtin_bit_cast(E4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)hi_p));
+    Frag r;
     r[0] = l4[0]; r[1] = l4[1]; r[2] = l4[2]; r[3] = l4[3];
     r[4] = h4[0]; r[5] = h4[1]; r[6] = h4[2]; r[7] = h4[3];
     return r;
@@ -551,7 +608,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
   // cost moves): the lane's key is visible from row offset c iff
   // mlo <= c < mlo + mspan (full tiles: every c). Rows past the end of the
   // range hold zeros in Q and dO (and in lse2 / delta), so they add nothing.
-  auto body = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd, int32_t mlo, uint32_t mspan) {
+  auto body = [&](const E *sq, const E *so, const float *sl, const float *sd, int32_t mlo, uint32_t mspan) {
     constexpr int KS = 2 * NS;      // score steps
     constexpr int KG = 4 * ND;      // gradient steps
     constexpr int PFA = 3, PFT = 3;  // read-ahead distances (steps)
@@ -559,7 +616,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     static_assert(16 % NS == 0 && 16 / (2 * ND) == JS, "two probability slots per step");
     const float sl2 = p.scale_log2;
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dpv[2] = {f32x16{}, f32x16{}};
-    bf16x8 pb[2][2], db[2][2];  // [half][16-row part]: P and dS as bf16 B operands
+    Frag pb[2][2], db[2][2];  // [half][16-row part]: P and dS as B operands
     f32x4 l4[2], d4[2];         // row terms of the current 4-row group, by half
     // one probability (row c_row(j) of half sub): exp2(S scale log2e - lse2),
     // masked; dS = P (dP - delta)
@@ -573,15 +630,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
       const int c = sub * 32 + 8 * (j >> 2) + e;  // row offset from the lane's first row
       float ex = fast_exp2(__builtin_fmaf(sc[sub][j], sl2, -l4[sub][e]));
       if constexpr (MASK) ex = (uint32_t)(c - mlo) < mspan ? ex : 0.f;
-      pb[sub][j >> 3][j & 7] = (bf16)ex;
-      db[sub][j >> 3][j & 7] = (bf16)(ex * (dpv[sub][j] - d4[sub][e]));
+      pb[sub][j >> 3][j & 7] = (E)ex;
+      db[sub][j >> 3][j & 7] = (E)(ex * (dpv[sub][j] - d4[sub][e]));
     };
-    bf16x8 fq[KS], fo[KS];  // A fragments by score step (each live for PFA steps)
+    Frag fq[KS], fo[KS];  // A fragments by score step (each live for PFA steps)
     auto load_a = [&](int k) {
       fq[k] = afrag(sq, k / NS, k % NS);
       fo[k] = afrag(so, k / NS, k % NS);
     };
-    bf16x8 tq[KG], to[KG];  // transposed A fragments by gradient step
+    Frag tq[KG], to[KG];  // transposed A fragments by gradient step
     auto load_t = [&](int k) {
       const int sub = k / (2 * ND), tt = (k / ND) % 2, dt = k % ND;
       to[k] = trfrag(so, sub * 32, tt, dt);
@@ -617,7 +674,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     }
   };
 
-  auto compute = [&](const bf16 *sq, const bf16 *so, const float *sl, const float *sd) {
+  auto compute = [&](const E *sq, const E *so, const float *sl, const float *sd) {
     const int32_t qt = cqt;
     advance(ch, cqt);
     if (!wave_on) return;
@@ -645,7 +702,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
     compute(sQ1, sO1, sL1, sD1);
     __syncthreads();
   }
-  if (!key_ok) return;
+  if (!key_ok) return true;
   float *dkr = p.dk + (int64_t)key * p.dk_st + (int64_t)hk * p.dk_sh;
   float *dvr = p.dv + (int64_t)key * p.dv_st + (int64_t)hk * p.dv_sh;
 #pragma unroll
@@ -664,6 +721,28 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdPara
       b.x += dv[dt][4 * j4]; b.y += dv[dt][4 * j4 + 1]; b.z += dv[dt][4 * j4 + 2]; b.w += dv[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dvr + d0) = b;
     }
+  return true;
+}
+
+template <int D, bool MASK>
+__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void dkdv_bf16_kernel(BwdParams p) {
+  using QT = std::conditional_t<D == 128, SwzTile128, PadTile<D, D / 8 + 5>>;
+  constexpr int QB = kBwdBQ;
+  __shared__ __attribute__((aligned(1024))) bf16 sQ0[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sO0[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sQ1[QT::ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 sO1[QT::ELEMS];
+  __shared__ __attribute__((aligned(16))) float sL0[QB];
+  __shared__ __attribute__((aligned(16))) float sD0[QB];
+  __shared__ __attribute__((aligned(16))) float sL1[QB];
+  __shared__ __attribute__((aligned(16))) float sD1[QB];
+  const int hkv_count = p.hq / p.group;
+  const int cap = gridDim.x / hkv_count;
+  if (xcd_block() % cap >= *p.count) return;
+  if (p.q16 && *p.h16_flag == 0 &&
+      dkdv_run<D, MASK, f16>(p, (f16 *)sQ0, (f16 *)sO0, (f16 *)sQ1, (f16 *)sO1, sL0, sD0, sL1, sD1))
+    return;
+  dkdv_run<D, MASK, bf16>(p, sQ0, sO0, sQ1, sO1, sL0, sD0, sL1, sD1);
 }
 
 // MASK = false: launches without a causal or window mask; only the keys past
@@ -894,6 +973,7 @@ hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   p.dv = a.dv; p.dv_st = a.dv_st; p.dv_sh = a.dv_sh;
   p.set_q = a.set_q ? 1 : 0;
   p.set_kv = a.set_kv ? 1 : 0;
+  p.q16 = a.q16; p.do16 = a.do16; p.h16_flag = a.h16_flag;
   if (a.dtype == 0) {
     if (a.head_dim == 128) return launch_bwd_t<bf16, 128>(p, a, which, s);
     return launch_bwd_t<bf16, 64>(p, a, which, s);
@@ -902,11 +982,21 @@ hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s) {
   return launch_bwd_t<float, 64>(p, a, which, s);
 }
 
-hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s) {
+hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s, int32_t *h16_flag) {
   if (n <= 0) return hipSuccess;
   int64_t b = (n + 255) / 256;
   if (b > 8192) b = 8192;
-  hipLaunchKernelGGL(lse2_kernel, dim3((unsigned)b), dim3(256), 0, s, lse, lse2, n);
+  hipLaunchKernelGGL(lse2_kernel, dim3((unsigned)b), dim3(256), 0, s, lse, lse2, n, h16_flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_half_copy(const HalfCopyArgs &a, hipStream_t s) {
+  const int64_t pieces = a.n * a.h * (a.d / 8);
+  if (pieces <= 0) return hipSuccess;
+  int64_t b = (pieces + 255) / 256;
+  if (b > 256 * 16) b = 256 * 16;
+  hipLaunchKernelGGL(half_copy_kernel, dim3((unsigned)b), dim3(256), 0, s, (const bf16 *)a.q, a.q_st, a.q_sh,
+                     (const bf16 *)a.dout, a.do_st, a.do_sh, (f16 *)a.q16, (f16 *)a.do16, a.n, a.h, a.d, a.flag);
   return hipGetLastError();
 }
 

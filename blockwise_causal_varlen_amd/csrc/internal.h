@@ -229,9 +229,25 @@ struct BwdArgs {
   SchedBufs ksched;   // tiles of key rows (dK/dV kernel)
   int64_t q_items, k_items;
   bool set_q = false, set_kv = false;  // store the gradients instead of adding to them
+  // f16 copies of q and dout (launch_half_copy) and their range flag; NULL:
+  // the dK/dV kernel runs on the bf16 inputs
+  const void *q16 = nullptr, *do16 = nullptr;
+  const int32_t *h16_flag = nullptr;
 };
-hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s);
-hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s);  // 0: dK/dV, 1: dQ
+hipError_t launch_bwd(const BwdArgs &a, int which, hipStream_t s);  // 0: dK/dV, 1: dQ
+// lse2 = lse * log2(e) (+inf where lse = -inf); also zeroes *h16_flag when given
+hipError_t launch_lse2(const float *lse, float *lse2, int64_t n, hipStream_t s, int32_t *h16_flag = nullptr);
+// f16 copies of bf16 q and dout [n, h, d] into contiguous buffers; sets *flag
+// when a value does not fit f16 (the flag is zeroed by launch_lse2 first)
+struct HalfCopyArgs {
+  const void *q, *dout;
+  int64_t q_st, q_sh, do_st, do_sh;
+  void *q16, *do16;
+  int64_t n;
+  int32_t h, d;
+  int32_t *flag;
+};
+hipError_t launch_half_copy(const HalfCopyArgs &a, hipStream_t s);
 
 // Zero the rows of an f32 [n, h, d] tensor that a block with this view does
 // not write: rows outside every document, and (view 1 / 2) the back / front

@@ -189,3 +189,35 @@ def test_window_edges(gpu_lib, window):
                       L.mask(**mk))
     torch.cuda.synchronize()
     check_bwd(got, rb, f"window {window}")
+
+
+@pytest.mark.parametrize("where", ["k", "dout"])
+def test_bwd_values_beyond_f16_range(gpu_lib, where):
+    """The dK/dV kernel runs its products in f16 (inputs converted exactly,
+    P and dS rounded to f16) unless a value does not fit f16: one k entry of
+    7e4 sends that key's workgroup to the bf16 inputs, one dout entry of 7e4
+    sends every workgroup there. OUTSIDE THE STATED BOUND: such inputs make
+    gradients of order 1e4-1e5, so the gradients are held to the bf16
+    rounding floor max(2e-2, 2^-8 max|ref|) (forward out / lse keep theirs)."""
+    L = gpu_lib
+    lens = [200, 77, 129]
+    cu_q, cu_k, q, k, v, dout = case(lens, lens, 4, 2, 128, seed=11)
+    if where == "k":
+        k[50, 1, 3] = 7.0e4
+        q[:, :, 3] = 0.0  # the scores stay finite and ordinary
+    else:
+        dout[120, 2, 7] = 7.0e4
+    scale = 1.0 / math.sqrt(128)
+    mk = dict(causal=True)
+    say(f"beyond f16: {where}")
+    ro, rl = O.block_forward(q, k, v, cu_q, cu_k, scale, **mk)
+    out, lse = L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu_q, cu_k, max(lens), max(lens), scale, L.mask(**mk))
+    torch.cuda.synchronize()
+    check_fwd(out, lse, ro, rl, f"beyond f16 {where}")
+    rb = O.block_backward(dout, q, k, v, out.cpu(), lse.cpu(), cu_q, cu_k, scale, **mk)
+    got = L.block_bwd(dout.cuda(), q.cuda(), k.cuda(), v.cuda(), out, lse, cu_q, cu_k, max(lens), max(lens), scale,
+                      L.mask(**mk))
+    torch.cuda.synchronize()
+    for name, g in zip(("dq", "dk", "dv"), got):
+        assert torch.isfinite(g).all(), f"{name}: non-finite values"
+    check_bwd(got, rb, f"beyond f16 {where}", rel=2.0 ** -8)
