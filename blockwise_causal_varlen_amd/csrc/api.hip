@@ -571,6 +571,67 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
                         lse, workspace, workspace_bytes, stream, nullptr);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The no-allocation forward's workspace: a file-scope device array, one copy
+// per GPU. In host code `scratch` names a host-side stand-in, not the device
+// copy: kernels get the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device ordinal -> that device's copy of scratch
+
+attn_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_ERR_UNSUPPORTED, "device ordinal %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p || ((uintptr_t)p) % 256) return fail(ATTN_ERR_HIP, "scratch array address not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_block_fwd_noalloc(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, const attn_mask *mask, float scale,
+                                   const attn_tensor *out, float *lse, void *stream) {
+  constexpr size_t kMax = ATTN_NOALLOC_SCRATCH_BYTES;
+  // the plan attn_block_fwd would make; without the automatic key split of
+  // small grids when its partials do not fit the array
+  Problem P;
+  TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, true));
+  bool split = true;
+  size_t need = fwd_ws_bytes(P, num_seqs);
+  if (need > kMax && P.nsplit > 0 && !(mask && mask->seg_size > 0)) {
+    TRY(plan_fwd(q, k, v, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, false));
+    split = false;
+    need = fwd_ws_bytes(P, num_seqs);
+  }
+  if (need > kMax)
+    return fail(ATTN_ERR_WORKSPACE,
+                "attn_block_fwd_noalloc: this call needs %zu bytes of workspace; its array holds at most %zu "
+                "(use attn_block_fwd with a caller workspace)", need, kMax);
+  void *ws = nullptr;
+  TRY(scratch_of_current_device(&ws));
+  return block_fwd_impl(q, k, v, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, mask, scale, out,
+                        lse, ws, kMax, stream, nullptr, nullptr, split);
+}
+
 attn_status attn_merge_out_lse(const attn_tensor *out, float *lse, const attn_tensor *block_out,
                                const float *block_lse, const int32_t *cu_seqlens, int32_t num_seqs,
                                uint32_t q_view, float *block_weight, const attn_tensor *final_out, int32_t init,

@@ -65,6 +65,7 @@ _SIGS = {
     "attn_workspace_size": (C.c_int, [C.c_int, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
     "attn_workspace_bytes": (C.c_int, [C.c_int, T, T, I32, I32, I32, M, C.POINTER(SZ)]),
     "attn_block_fwd": (C.c_int, [T, T, T, P, P, I32, I32, I32, M, F, T, P, P, SZ, P]),
+    "attn_block_fwd_noalloc": (C.c_int, [T, T, T, P, P, I32, I32, I32, M, F, T, P, P]),
     "attn_merge_out_lse": (C.c_int, [T, P, T, P, P, I32, U32, P, T, I32, P]),
     "attn_merge_n": (C.c_int, [I32, T, C.POINTER(P), T, P, P]),
     "attn_bwd_delta": (C.c_int, [T, T, P, P]),
@@ -242,6 +243,17 @@ def block_fwd(q, k, v, cu_q, cu_k, max_q, max_k, scale, m: AttnMask | None = Non
     wp, wn = _aligned(ws)
     _call("attn_block_fwd", C.byref(qd), C.byref(kd), C.byref(vd), cq.data_ptr(), ck.data_ptr(), ns, max_q, max_k,
           _ref(m), scale, C.byref(desc(out)), lse.data_ptr(), wp, wn, _stream(stream))
+    return out, lse
+
+
+def block_fwd_noalloc(q, k, v, cu_q, cu_k, max_q, max_k, scale, m: AttnMask | None, out, lse, stream=None,
+                      k_desc=None, v_desc=None):
+    """attn_block_fwd_noalloc on torch tensors: the caller provides out and lse
+    and device cu_seqlens; the library uses its own device array as workspace."""
+    qd, kd, vd = desc(q), k_desc or desc(k), v_desc or desc(v)
+    ns = cu_q.numel() - 1
+    _call("attn_block_fwd_noalloc", C.byref(qd), C.byref(kd), C.byref(vd), cu_q.data_ptr(), cu_k.data_ptr(), ns, max_q,
+          max_k, _ref(m), scale, C.byref(desc(out)), lse.data_ptr(), _stream(stream))
     return out, lse
 
 

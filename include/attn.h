@@ -199,6 +199,29 @@ attn_status attn_block_fwd(const attn_tensor *q, const attn_tensor *k, const att
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_block_fwd_noalloc -- attn_block_fwd for callers that cannot allocate
+ * device memory: code under hipGraph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments and results as attn_block_fwd,
+ * without the workspace: the library keeps one device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES per GPU (its address looked up on the first call
+ * on that GPU, held until the process ends) and never allocates or frees.
+ * A call whose plan needs more workspace than the array holds (paged keys
+ * with many pages, segment partials of large calls) fails with
+ * ATTN_ERR_WORKSPACE before launching anything; when only the automatic key
+ * split of small grids does not fit, the call runs without it (same result up
+ * to rounding). Every call on one GPU uses the same array and nothing in it
+ * needs to start at zero; calls that overlap in time on one GPU (on different
+ * streams or threads) race on it and must not be issued; calls on one stream
+ * are ordered by it.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+attn_status attn_block_fwd_noalloc(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
+                                   const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                                   int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   const attn_mask *mask, float scale,
+                                   const attn_tensor *out, float *lse, void *stream);
+
+/*
  * attn_merge_out_lse -- merge one block's partial into the running state.
  * [ZZ] `update_out_and_lse` / [RING] `_update_out_and_lse`, `_init_out_and_lse`:
  *     lse' = ln(e^lse + e^block_lse)
