@@ -166,6 +166,85 @@ def traffic_summary(fetch_csv, write_csv, out_path, command):
     print("\n".join(lines))
 
 
+# Counters of one rocprofv3 --pmc pass each (at most 8 SQ and 2 GRBM counters a pass)
+COUNTER_PASSES = [
+    ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+     "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_INSTS_SALU"],
+    ["GRBM_GUI_ACTIVE", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+     "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "SQ_LDS_BANK_CONFLICT"],
+]
+SIMDS = 256 * 4
+XCDS = 8  # GRBM_GUI_ACTIVE comes summed over the 8 XCDs (each counts its active cycles)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "zigzag_cp8_rank3_fwd_bwd_counters.txt")
+
+
+def load_counters(kernel):
+    """MFMA-busy fraction and instruction mix of a kernel from the committed
+    rocprofv3 counter summary, if it matches the current kernel sources."""
+    path = COUNTERS_FILE
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#") or "=" not in line:
+            continue
+        k, v = line.split("=", 1)
+        rec[k.strip()] = v.strip()
+    if rec.get("sources") != sources_digest():
+        return None
+    keys = ("mfma_busy", "valu_per_mfma", "trans_per_mfma", "lds_per_mfma", "coexec_of_mfma_busy", "wait_lds_of_wave",
+            "wait_any_of_wave", "lds_bank_conflict_of_lds_active")
+    out = {k: float(rec[f"{kernel}.{k}"]) for k in keys if f"{kernel}.{k}" in rec}
+    return out or None
+
+
+def counter_summary(csvs, out_path, command):
+    """Per-kernel means of the rocprofv3 --pmc passes (COUNTER_PASSES), and the
+    derived MFMA-busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles
+    of one XCD, GRBM_GUI_ACTIVE / 8, times 1024 SIMDs: the share of the SIMDs'
+    cycles at the clock the kernel ran at), VALU / transcendental / LDS
+    instructions per MFMA, co-execution and wait fractions."""
+    import csv
+    import statistics
+    vals = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            for key, tname in TRAFFIC_KERNELS.items():
+                if key in name:
+                    vals.setdefault(tname, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    break
+    lines = ["# rocprofv3 counters per launch (mean over the profiled launches) and derived ratios",
+             "# commands:"] + ["#   " + c for c in command] + [f"sources = {sources_digest()}"]
+    for tname in sorted(vals):
+        c = {k: statistics.mean(v) for k, v in vals[tname].items()}
+        for k in sorted(c):
+            lines.append(f"{tname}.{k} = {c[k]:.6g}")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        mf = c.get("SQ_INSTS_MFMA")
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            lines.append(f"{tname}.mfma_busy = {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui / XCDS * SIMDS):.4f}")
+        if mf:
+            for src, dst in (("SQ_INSTS_VALU", "valu_per_mfma"), ("SQ_INSTS_VALU_TRANS_F32", "trans_per_mfma"),
+                             ("SQ_INSTS_LDS", "lds_per_mfma")):
+                if src in c:
+                    lines.append(f"{tname}.{dst} = {c[src] / mf:.3f}")
+        if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+            lines.append(f"{tname}.coexec_of_mfma_busy = "
+                         f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}")
+        if c.get("SQ_WAVE_CYCLES"):
+            for src, dst in (("SQ_WAIT_INST_LDS", "wait_lds_of_wave"), ("SQ_WAIT_INST_ANY", "wait_any_of_wave")):
+                if src in c:
+                    lines.append(f"{tname}.{dst} = {c[src] / c['SQ_WAVE_CYCLES']:.4f}")
+        if c.get("SQ_ACTIVE_INST_LDS") and "SQ_LDS_BANK_CONFLICT" in c:
+            lines.append(f"{tname}.lds_bank_conflict_of_lds_active = "
+                         f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_ACTIVE_INST_LDS']:.4f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def timed_steps(step, steps, warmup, torch, lib, timing=True):
     for _ in range(warmup):
         step()
@@ -220,13 +299,18 @@ def headline(args, torch, lib, I, W):
     tflops = (fwd_f + bwd_f) / sec / 1e12
     doc_lens = wl.doc_lens
     rows_all = sum(L_ // cp for L_ in doc_lens)
-    delta_bytes = rows_all * hq * (256 + 256 + 4)
+    # the delta pass reads dout and out (bf16) and writes delta; with bf16
+    # inputs it also reads q and writes the f16 copies of q and dout
+    delta_bytes = rows_all * hq * (2 * d * 2 + 4 + (d * 2 + 2 * d * 2 if case.q.dtype == torch.bfloat16 else 0))
     kernels = {
         "attn_fwd": roofline("attn_fwd", fwd_f, kt, args.steps, "mfma", load_traffic("attn_fwd")),
         "attn_dkdv": roofline("attn_dkdv", 8 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dkdv")),
         "attn_dq": roofline("attn_dq", 2 * d * hq * pairs, kt, args.steps, "mfma", load_traffic("attn_dq")),
         "attn_delta": roofline("attn_delta", delta_bytes, kt, args.steps, "hbm", load_traffic("attn_delta")),
     }
+    for name, rec in kernels.items():
+        if rec is not None:
+            rec["counters"] = load_counters(name)
     times = {k: v[1] for k, v in kt.items()}
     dominant = max((k for k in kernels if kernels[k]), key=lambda k: times.get(k, 0.0))
     cfg = {"workload": "zigzag cp=8, virtual rank 3 of 131072 packed tokens (16384 local rows), fwd 8 blocks "
@@ -423,8 +507,20 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc counter CSVs into profiles/traffic.txt")
     ap.add_argument("--traffic-command", action="append", default=[],
-                    help="with --traffic-summary: a command line to record in the summary")
+                    help="with --traffic-summary / --counter-summary: a command line to record in the summary")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="host only: turn rocprofv3 --pmc counter CSVs (the passes of COUNTER_PASSES) into "
+                         "the counter summary under profiles/")
+    ap.add_argument("--print-counter-passes", action="store_true",
+                    help="print the counter list of each --pmc pass, one line each")
     args = ap.parse_args()
+    if args.print_counter_passes:
+        for p in COUNTER_PASSES:
+            print(" ".join(p))
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary, COUNTERS_FILE, args.traffic_command)
+        return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
                         os.path.join(ROOT, "profiles", "traffic.txt"), args.traffic_command)

@@ -821,7 +821,14 @@ attn_status attn_out_transpose(const attn_tensor *src, void *dst, void *stream) 
   return hip_check(timed("attn_transpose", s, [&] { return launch_out_transpose(a, s); }), "transpose kernel");
 }
 
-attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// delta, and with h16 (bf16 q and dout) the f16 copies of q and dout in the
+// same pass over dout
+attn_status bwd_delta_impl(const attn_tensor *dout, const attn_tensor *out, float *delta, const attn_tensor *q,
+                           const HalfCopies *h16, void *stream) {
   TRY(check_tensor(dout, "dout"));
   TRY(check_tensor(out, "out"));
   TRY(check_hd(out->head_dim));
@@ -832,8 +839,22 @@ attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, floa
   a.dout = dout->data; a.dtype_do = dout->dtype; a.do_st = dout->stride_tok; a.do_sh = dout->stride_head;
   a.out = out->data; a.dtype_o = out->dtype; a.o_st = out->stride_tok; a.o_sh = out->stride_head;
   a.delta = delta; a.n = out->n_tok; a.h = out->n_head; a.d = out->head_dim;
+  if (h16 && h16->q16) {
+    if (!q || q->dtype != ATTN_BF16 || dout->dtype != ATTN_BF16 || q->n_tok != out->n_tok || q->n_head != out->n_head)
+      return fail(ATTN_ERR_INVALID, "internal: f16 copies need bf16 q and dout shaped like out");
+    a.q = q->data; a.q_st = q->stride_tok; a.q_sh = q->stride_head;
+    a.q16 = h16->q16; a.do16 = h16->do16; a.h16_flag = h16->flag;
+  }
   hipStream_t s = (hipStream_t)stream;
   return hip_check(timed("attn_delta", s, [&] { return launch_delta(a, s); }), "delta kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd_delta(const attn_tensor *dout, const attn_tensor *out, float *delta, void *stream) {
+  return bwd_delta_impl(dout, out, delta, nullptr, nullptr, stream);
 }
 
 }  // extern "C"
@@ -912,18 +933,22 @@ attn_status block_bwd_impl(const attn_tensor *dout, const attn_tensor *q, const 
     w += align256(sched_bytes(capk));
     float *l2 = (float *)w;
     w += align256((size_t)q->n_head * q->n_tok * 4);
+    float *dl = nullptr;
     if (!delta) {
-      float *dl = (float *)w;
+      dl = (float *)w;
       w += align256((size_t)q->n_head * q->n_tok * 4);
-      TRY(attn_bwd_delta(dout, out, dl, stream));
-      delta = dl;
     }
     if (q->dtype == ATTN_BF16) h16 = half_carve(w, q->n_tok, q->n_head, q->head_dim);
+    // lse2 first: it zeroes the f16 range flag the copies may set
     TRY(hip_check(timed("attn_lse2", s, [&] { return launch_lse2(lse, l2, q->n_head * q->n_tok, s, h16.flag); }),
                   "lse2"));
     lse2 = l2;
-    if (h16.q16)
+    if (dl) {
+      TRY(bwd_delta_impl(dout, out, dl, q, &h16, stream));  // with the f16 copies in the same pass
+      delta = dl;
+    } else if (h16.q16) {
       TRY(hip_check(timed("attn_half_copy", s, [&] { return launch_half_copies(h16, q, dout, s); }), "f16 copies"));
+    }
     const SchedJob jobs[2] = {
         {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kFwdBN, 0, 1, sq},
         {cu_seqlens_q, cu_seqlens_k, num_seqs, q->n_tok, k->n_tok, md, kBwdTile, kBwdBQ, 1, 1, sk}};
@@ -1209,15 +1234,14 @@ attn_status run_ring_bwd(int32_t cp, int32_t rank, int32_t n_steps, StepMask mk,
                        &masks[s], scale, dq, &dk_loc[src], &dv_loc[src], nullptr, 0, stream, &none, false, false,
                        true));
   }
-  TRY(attn_bwd_delta(dout, out, delta, stream));
   std::vector<BwdPre> pre(kinds.size());
-  if (num_seqs > 0 && q->n_tok > 0) {
-    HalfCopies h16;
-    if (q->dtype == ATTN_BF16) h16 = half_carve(w + L.h16_off, q->n_tok, q->n_head, q->head_dim);
+  HalfCopies h16;
+  if (num_seqs > 0 && q->n_tok > 0 && q->dtype == ATTN_BF16) h16 = half_carve(w + L.h16_off, q->n_tok, q->n_head, q->head_dim);
+  if (num_seqs > 0 && q->n_tok > 0)  // lse2 first: it zeroes the f16 range flag the delta pass may set
     TRY(hip_check(timed("attn_lse2", st, [&] { return launch_lse2(lse, lse2, q->n_head * q->n_tok, st, h16.flag); }),
                   "lse2"));
-    if (h16.q16)
-      TRY(hip_check(timed("attn_half_copy", st, [&] { return launch_half_copies(h16, q, dout, st); }), "f16 copies"));
+  TRY(bwd_delta_impl(dout, out, delta, q, &h16, stream));  // delta and the f16 copies in one pass
+  if (num_seqs > 0 && q->n_tok > 0) {
     for (auto &pr : pre) pr.h16 = h16;
     SchedJob jobs[2 * kRingKinds];
     for (size_t i = 0; i < kinds.size(); ++i) {

@@ -167,6 +167,12 @@ struct DeltaArgs {
   const void *out; int32_t dtype_o; int64_t o_st, o_sh;
   float *delta;
   int64_t n, h, d;
+  // optional, bf16 q and dout only: also write their f16 copies ([n, h, d]
+  // contiguous) and set *h16_flag where a value does not fit f16 (the flag is
+  // zeroed before, by launch_lse2)
+  const void *q = nullptr; int64_t q_st = 0, q_sh = 0;
+  void *q16 = nullptr, *do16 = nullptr;
+  int32_t *h16_flag = nullptr;
 };
 hipError_t launch_delta(const DeltaArgs &a, hipStream_t s);
 
