@@ -328,10 +328,18 @@ def other_rows(args, torch, lib, I, W):
     # packed varlen forward, 4 zig-zag ranks (all of them)
     c2 = I.cfg2()
     w2 = W.ZigzagWorkload(c2)
-    sec, kt = timed_steps(w2.forward, steps, args.warmup, torch, lib)
     f = w2.fwd_flops()
+    # the 4 virtual ranks on 4 streams (each rank's 4 blocks its own launches) ...
+    sec, kt = timed_steps(w2.forward, steps, args.warmup, torch, lib)
     rows["packed_varlen_fwd_cp4"] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12, "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+                                     "ranks": "4 streams, 16 forward launches",
                                      "fwd_kernel": roofline("attn_fwd", f, kt, steps, "mfma")}
+    # ... and batched: each ring step's 4 blocks in one launch
+    sec, kt = timed_steps(w2.forward_batched, steps, args.warmup, torch, lib)
+    rows["packed_varlen_fwd_cp4_batched"] = {"ms": sec * 1e3, "TFLOP/s": f / sec / 1e12,
+                                             "frac": f / sec / 1e12 / PEAK_BF16_TFLOPS,
+                                             "ranks": "one stream, 4 forward launches (one per ring step)",
+                                             "fwd_kernel": roofline("attn_fwd", f, kt, steps, "mfma")}
     del w2, c2
     for window in (0, 4096):
         c4 = I.cfg4(window=window)

@@ -535,8 +535,8 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     // no fill: every query tile has one item per part, and a part that sees
     // no key still writes lse = -inf for its rows; rows of no tile are not merged
   }
-  if (defer) {  // the caller launches it with others (writes to the given parts only)
-    if (!po) return fail(ATTN_ERR_INVALID, "internal: a deferred forward needs its parts buffer");
+  if (defer) {  // the caller launches it with others (writes to the given parts / its own rows only)
+    if (!po && !fm) return fail(ATTN_ERR_INVALID, "internal: a deferred forward needs its parts buffer");
     *defer = a;
     return ok();
   }
@@ -1289,6 +1289,98 @@ attn_status attn_zigzag_fwd(int32_t cp, int32_t rank, const attn_tensor *q, cons
                             float *lse, void *workspace, size_t workspace_bytes, void *stream) {
   return run_ring_fwd(cp, rank, cp, zigzag_mask, q, k_loc, v_loc, cu_local, num_seqs, max_seqlen_local, scale, out_acc,
                       out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_zigzag_fwd_ranks(int32_t cp, int32_t n_ranks, const int32_t *ranks, const attn_tensor *q,
+                                  const attn_tensor *k_loc, const attn_tensor *v_loc, const int32_t *cu_local,
+                                  int32_t num_seqs, int32_t max_seqlen_local, float scale, const attn_tensor *out_acc,
+                                  const attn_tensor *out, float *const *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  if (n_ranks < 1 || n_ranks > cp) return fail(ATTN_ERR_INVALID, "need 1 <= n_ranks <= cp");
+  if (!q || !out_acc || !out || !lse) return fail(ATTN_ERR_NULL, "NULL rank array");
+  std::vector<int32_t> rk(n_ranks);
+  for (int i = 0; i < n_ranks; ++i) {
+    rk[i] = ranks ? ranks[i] : i;
+    if (rk[i] < 0 || rk[i] >= cp) return fail(ATTN_ERR_INVALID, "ranks[%d] = %d outside [0, cp)", i, rk[i]);
+    for (int j = 0; j < i; ++j)
+      if (rk[j] == rk[i]) return fail(ATTN_ERR_INVALID, "rank %d listed twice", rk[i]);
+    if (q[i].n_tok != q[0].n_tok || q[i].n_head != q[0].n_head || q[i].head_dim != q[0].head_dim ||
+        q[i].dtype != q[0].dtype)
+      return fail(ATTN_ERR_SHAPE, "every rank's q must be shaped like q[0]");
+  }
+  TRY(check_tensor(&q[0], "q"));
+  TRY(check_ring_args(cp, rk[0], &q[0], k_loc, v_loc));
+  const RingLayout L = ring_layout(&q[0], &k_loc[0], num_seqs);
+  const size_t slice = align256(L.total > L.btotal ? L.total : L.btotal);
+  if (!workspace || workspace_bytes < slice * n_ranks)
+    return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes needed (n_ranks x attn_zigzag_workspace_size)",
+                slice * n_ranks);
+  if (((uintptr_t)workspace) % 256) return fail(ATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  char *w = (char *)workspace;
+  const bool batch = can_fuse_merge(&q[0], max_seqlen_local, nullptr) && num_seqs > 0 && q[0].n_tok > 0;
+  if (!batch) {  // f32 inputs, one query a document, or nothing to do: the ranks one after another
+    for (int i = 0; i < n_ranks; ++i)
+      TRY(run_ring_fwd(cp, rk[i], cp, zigzag_mask, &q[i], k_loc, v_loc, cu_local, num_seqs, max_seqlen_local, scale,
+                       &out_acc[i], &out[i], lse[i], w + i * slice, slice, stream));
+    return ok();
+  }
+  hipStream_t st = (hipStream_t)stream;
+  // every rank's arguments checked, and its block kinds' schedules computed (all ranks' in few launches)
+  std::vector<std::vector<attn_mask>> masks(n_ranks), kinds(n_ranks);
+  std::vector<std::vector<int>> kind_of(n_ranks);
+  std::vector<std::vector<SchedBufs>> sch(n_ranks);
+  std::vector<SchedJob> jobs;
+  std::vector<int> last_front(n_ranks, -1), last_back(n_ranks, -1);
+  for (int i = 0; i < n_ranks; ++i) {
+    TRY(check_ring_args(cp, rk[i], &q[i], k_loc, v_loc));
+    TRY(check_tensor(&out_acc[i], "out_acc"));
+    if (out_acc[i].dtype != ATTN_F32) return fail(ATTN_ERR_DTYPE, "out_acc must be f32");
+    TRY(check_tensor(&out[i], "out"));
+    if (!lse[i]) return fail(ATTN_ERR_NULL, "lse[%d] is NULL", i);
+    if (!cu_local) return fail(ATTN_ERR_NULL, "cu_seqlens is NULL");
+    Problem shp;
+    shp.n_q = q[i].n_tok; shp.hq = q[i].n_head; shp.d = q[i].head_dim;
+    TRY(check_out(&out_acc[i], shp, "out_acc"));
+    TRY(ring_kinds(cp, rk[i], cp, zigzag_mask, masks[i], kind_of[i], kinds[i]));
+    sch[i].resize(kinds[i].size());
+    for (size_t k = 0; k < kinds[i].size(); ++k) {
+      TRY(check_mask(&kinds[i][k]));
+      sch[i][k] = sched_carve(w + i * slice + L.fsched_off + k * L.fsched_stride, L.fcap);
+      jobs.push_back(SchedJob{cu_local, cu_local, num_seqs, q[i].n_tok, k_loc[0].n_tok, mask_dev(&kinds[i][k]), kFwdBM,
+                              kFwdBN, 0, 1, sch[i][k]});
+    }
+    for (int s = 0; s < cp; ++s) {
+      if (masks[i][s].q_view != ATTN_VIEW_BACK) last_front[i] = s;
+      if (masks[i][s].q_view != ATTN_VIEW_FRONT) last_back[i] = s;
+    }
+  }
+  for (size_t j0 = 0; j0 < jobs.size(); j0 += kMaxSchedJobs) {
+    const int nj = (int)(jobs.size() - j0 < (size_t)kMaxSchedJobs ? jobs.size() - j0 : kMaxSchedJobs);
+    TRY(hip_check(timed("attn_sched", st, [&] { return launch_schedules(jobs.data() + j0, nj, st); }), "scheduler"));
+  }
+  // step by step: the ranks' blocks of one step in one launch (a step's
+  // blocks are all causal (step 0) or all unmasked, of one shape)
+  std::vector<FwdArgs> fa(n_ranks);
+  for (int s = 0; s < cp; ++s) {
+    for (int i = 0; i < n_ranks; ++i) {
+      const int src = ((rk[i] - s) % cp + cp) % cp;
+      const FusedMerge fm{&out_acc[i], s > 0, (s == last_front[i] ? 1 : 0) | (s == last_back[i] ? 2 : 0)};
+      TRY(block_fwd_impl(&q[i], &k_loc[src], &v_loc[src], cu_local, cu_local, num_seqs, max_seqlen_local,
+                         max_seqlen_local, &masks[i][s], scale, &out[i], lse[i], w + i * slice + L.fwd_off,
+                         L.fsched_off - L.fwd_off, stream, &fm, &sch[i][kind_of[i][s]], false, nullptr, &fa[i]));
+    }
+    for (int i0 = 0; i0 < n_ranks; i0 += kMaxFwdBatch) {
+      const int nb = n_ranks - i0 < kMaxFwdBatch ? n_ranks - i0 : kMaxFwdBatch;
+      if (fwd_batchable(fa.data() + i0, nb)) {
+        TRY(hip_check(timed("attn_fwd", st, [&] { return launch_fwd_batch(fa.data() + i0, nb, st); }),
+                      "forward kernel"));
+      } else {
+        for (int i = i0; i < i0 + nb; ++i)
+          TRY(hip_check(timed("attn_fwd", st, [&] { return launch_fwd(fa[i], st); }), "forward kernel"));
+      }
+    }
+  }
+  return ok();
 }
 
 attn_status attn_zigzag_bwd(int32_t cp, int32_t rank, const attn_tensor *dout, const attn_tensor *q,

@@ -78,6 +78,7 @@ _SIGS = {
     "attn_zigzag_shard": (C.c_int, [T, P, I32, I32, I32, I32, T, P]),
     "attn_zigzag_workspace_size": (C.c_int, [I32, T, T, I32, I32, C.POINTER(SZ)]),
     "attn_zigzag_fwd": (C.c_int, [I32, I32, T, T, T, P, I32, I32, F, T, T, P, P, SZ, P]),
+    "attn_zigzag_fwd_ranks": (C.c_int, [I32, I32, P, T, T, T, P, I32, I32, F, T, T, C.POINTER(P), P, SZ, P]),
     "attn_zigzag_bwd": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P]),
     "attn_zigzag_bwd_ex": (C.c_int, [I32, I32, T, T, T, T, T, P, P, I32, I32, F, T, T, T, P, SZ, P, C.c_uint32]),
     "attn_ring_fwd": (C.c_int, [I32, I32, T, T, T, P, I32, I32, F, T, T, P, P, SZ, P]),
@@ -412,6 +413,29 @@ class RingRunner:
               self.lse.data_ptr(), self.cu.data_ptr(), self.ns, self.max_local, self.scale, C.byref(self.dqd),
               self.dkd, self.dvd, self.wp, self.wn, _stream(stream), BWD_SET if set_grads else 0)
         return self.dq, self.dk, self.dv
+
+
+class ZigzagRanksForward:
+    """attn_zigzag_fwd_ranks over the RingRunners of several ranks of one ring
+    (their q, out_acc, out and lse): each step's blocks in one launch."""
+
+    def __init__(self, runners):
+        r0 = runners[0]
+        self.cp, self.n = r0.cp, len(runners)
+        self.ranks = (I32 * self.n)(*[r.rank for r in runners])
+        self.qd = (AttnTensor * self.n)(*[r.qd for r in runners])
+        self.oad = (AttnTensor * self.n)(*[r.oad for r in runners])
+        self.od = (AttnTensor * self.n)(*[r.od for r in runners])
+        self.lse = (P * self.n)(*[r.lse.data_ptr() for r in runners])
+        self.r0 = r0
+        slice_ = (r0.wn + 255) // 256 * 256
+        self.ws = _workspace(slice_ * self.n, r0.q.device)
+        self.wp, self.wn = _aligned(self.ws)
+
+    def forward(self, stream=None):
+        r0 = self.r0
+        _call("attn_zigzag_fwd_ranks", self.cp, self.n, self.ranks, self.qd, r0.kd, r0.vd, r0.cu.data_ptr(), r0.ns,
+              r0.max_local, r0.scale, self.oad, self.od, self.lse, self.wp, self.wn, _stream(stream))
 
 
 def kvp_fwd(q_shd, k_caches, v_caches, tables, cu_q, cu_k, max_q, max_k, scale, m: AttnMask, out=None, lse=None,

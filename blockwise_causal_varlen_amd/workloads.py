@@ -107,6 +107,13 @@ class ZigzagWorkload:
         self.streams = ({r: torch.cuda.Stream(device=device) for r in self.ranks}
                         if len(self.ranks) > 1 else None)
 
+    def forward_batched(self):
+        """All listed ranks' forwards through attn_zigzag_fwd_ranks: each ring
+        step's blocks of every rank in one launch (on the current stream)."""
+        if getattr(self, "_batched", None) is None:
+            self._batched = L.ZigzagRanksForward([self.runners[r] for r in self.ranks])
+        self._batched.forward()
+
     def _each_rank(self, fn):
         if self.streams is None:
             for r in self.ranks:

@@ -397,6 +397,27 @@ attn_status attn_zigzag_fwd(int32_t cp, int32_t rank, const attn_tensor *q,
                             float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_zigzag_fwd_ranks -- attn_zigzag_fwd of n_ranks virtual ranks of one
+ * ring together: at each step the ranks' blocks (each independent of the
+ * others given the K/V it holds, [ZZ] `zigzag_ring_flash_attn_varlen_forward`)
+ * run in one launch, which fills the chip when one rank's block alone cannot
+ * (small local shards). Results are those of attn_zigzag_fwd per rank.
+ *   ranks      host array of n_ranks distinct ranks in [0, cp) (NULL: 0 .. n_ranks-1)
+ *   q, out_acc, out  host arrays of n_ranks descriptors, one per listed rank
+ *              (every q shaped alike)
+ *   lse        host array of n_ranks device pointers
+ *   k_loc, v_loc, cu_local, num_seqs, max_seqlen_local, scale: as for attn_zigzag_fwd
+ * Workspace: n_ranks slices of attn_zigzag_workspace_size (each rounded up
+ * to 256 bytes), one per listed rank. bf16 inputs run batched (up to 8 ranks a
+ * launch); f32 inputs run the ranks one after another. 1 <= n_ranks <= cp.
+ */
+attn_status attn_zigzag_fwd_ranks(int32_t cp, int32_t n_ranks, const int32_t *ranks, const attn_tensor *q,
+                                  const attn_tensor *k_loc, const attn_tensor *v_loc, const int32_t *cu_local,
+                                  int32_t num_seqs, int32_t max_seqlen_local, float scale,
+                                  const attn_tensor *out_acc, const attn_tensor *out, float *const *lse,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * attn_zigzag_bwd -- rank `rank`'s zig-zag backward with the merged out/lse
  * ([ZZ] `zigzag_ring_flash_attn_varlen_backward`): delta once, then the cp
  * blocks of attn_zigzag_fwd in the same order, dq into `dq`, dk/dv of the

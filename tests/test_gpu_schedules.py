@@ -114,6 +114,37 @@ def test_zigzag_cfg2_forward_full(gpu_lib):
         check_lse("lse", wl.runners[r].lse.cpu(), rl)
 
 
+@pytest.mark.parametrize("which", ["cfg2", "small_f32_two_ranks"])
+def test_zigzag_forward_ranks_batched(gpu_lib, which):
+    """attn_zigzag_fwd_ranks: every ring step's blocks of the listed ranks in
+    one launch. cfg2 (8192 tokens, cp = 4, bf16): every element against the
+    oracle and bit-identical to the per-rank drivers; a small f32 ring with
+    two of its ranks listed out of order (run one after another)."""
+    if which == "cfg2":
+        case, ranks = inputs.cfg2(), None
+    else:
+        case, ranks = inputs.small_zigzag(512, 8, 120, 4, 2, 64, torch.float32, 4, seed=9), [3, 1]
+    cp = case.cp
+    wl = W.ZigzagWorkload(case, ranks=ranks)
+    wl.forward()
+    torch.cuda.synchronize()
+    ref = {r: (wl.runners[r].out.clone(), wl.runners[r].lse.clone()) for r in wl.ranks}
+    for r in wl.ranks:
+        wl.runners[r].out.fill_(7.0)
+        wl.runners[r].lse.fill_(9.0)
+    wl.forward_batched()
+    torch.cuda.synchronize()
+    oks, ovs = oracle_locals(case)
+    oqs = [O.zigzag_shard(case.q, case.cu, cp, r)[0] for r in range(cp)]
+    for r in wl.ranks:
+        say(f" rank {r}")
+        run = wl.runners[r]
+        assert torch.equal(run.out, ref[r][0]) and torch.equal(run.lse, ref[r][1]), "batched != per-rank driver"
+        ro, rl = O.zigzag_forward(oqs, oks, ovs, case.cu, cp, r, case.scale, check=False)
+        check("out", run.out.cpu(), ro, OUT_TOL)
+        check_lse("lse", run.lse.cpu(), rl)
+
+
 def _sample_rows(n_rows, cu_local, k, seed):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(n_rows, size=k, replace=False).tolist())
