@@ -166,6 +166,54 @@ def traffic_summary(fetch_csv, write_csv, out_path, command):
     print("\n".join(lines))
 
 
+TRACE_FILE = os.path.join(ROOT, "profiles", "zigzag_cp8_rank3_fwd_bwd_kernel_trace.md")
+
+
+def trace_summary(stats_csv, trace_csv, bench_json, out_path, command, timed_fraction):
+    """Kernel-trace summary of a rocprofv3 --kernel-trace --stats run over the
+    headline bench: the stats table (every dispatch), then each library
+    kernel's mean over the timed steps only (the last timed_fraction of its
+    dispatches), beside the mean launch duration the bench measured live with
+    hipEvents (bench_json: the JSON line of a bench.py run of the same sources)."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel trace: zig-zag cp=8 rank-3 step (131072 tokens, HQ=32, HKV=8, D=128, bf16), fwd + bwd", "",
+             "Commands (from the repository root, on one MI355X):", "", "```"] + command + ["```", "",
+             f"Sources digest {sources_digest()}. All dispatches of the profiled run (durations in microseconds):",
+             "", "| kernel | calls | total us | mean us | % |", "|---|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:16]:
+        name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        for key, tname in TRAFFIC_KERNELS.items():
+            if key in r["Kernel_Name"]:
+                per.setdefault(tname, []).append((int(r["Start_Timestamp"]),
+                                                  (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+                break
+    bench = {}
+    if bench_json:
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        bench = {k: v.get("mean_launch_us") for k, v in rec.get("kernels", {}).items() if v}
+        lines += ["", f"bench.py line used for the hipEvent column: {rec.get('value')} {rec.get('unit')}, "
+                      f"{rec.get('ms_per_step')} ms per step, sources {rec.get('sources')}."]
+    lines += ["", f"Per kernel, the mean over the timed steps (the last {timed_fraction:.2f} of its dispatches) "
+                  "beside the bench's hipEvent mean:", "",
+              "| kernel | rocprofv3 timed-step mean us | bench.py hipEvent mean us |", "|---|---:|---:|"]
+    for tname in ("attn_fwd", "attn_dkdv", "attn_dq", "attn_delta"):
+        if tname not in per:
+            continue
+        d = [x[1] for x in sorted(per[tname])]
+        timed = d[len(d) - max(1, round(len(d) * timed_fraction)):]
+        b = bench.get(tname)
+        lines.append(f"| {tname} | {statistics.mean(timed):.1f} | {b if b is not None else '-'} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # Counters of one rocprofv3 --pmc pass each (at most 8 SQ and 2 GRBM counters a pass)
 COUNTER_PASSES = [
     ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
@@ -515,10 +563,16 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc counter CSVs into profiles/traffic.txt")
     ap.add_argument("--traffic-command", action="append", default=[],
-                    help="with --traffic-summary / --counter-summary: a command line to record in the summary")
+                    help="with --traffic-summary / --counter-summary / --trace-summary: a command line to record in the summary")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="host only: turn rocprofv3 --pmc counter CSVs (the passes of COUNTER_PASSES) into "
                          "the counter summary under profiles/")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "BENCH_JSON"),
+                    help="host only: turn a rocprofv3 --kernel-trace --stats run of the headline (its "
+                         "kernel_stats and kernel_trace CSVs) and a bench.py JSON line into the kernel-trace "
+                         "summary under profiles/ (BENCH_JSON may be '-')")
+    ap.add_argument("--trace-timed-fraction", type=float, default=0.75,
+                    help="with --trace-summary: the share of each kernel's dispatches in the timed steps")
     ap.add_argument("--print-counter-passes", action="store_true",
                     help="print the counter list of each --pmc pass, one line each")
     args = ap.parse_args()
@@ -528,6 +582,11 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, COUNTERS_FILE, args.traffic_command)
+        return
+    if args.trace_summary:
+        st, tr, bj = args.trace_summary
+        trace_summary(st, tr, None if bj == "-" else bj, TRACE_FILE, args.traffic_command,
+                      args.trace_timed_fraction)
         return
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1],
