@@ -448,8 +448,8 @@ __global__ __launch_bounds__(256) void half_copy_kernel(const bf16 *q, int64_t q
 // E: the element type of the MFMA operands. f16 (q, dout from their f16
 // copies, k and v converted in registers; P and dS rounded to f16) unless a
 // value does not fit f16, then bf16 (the inputs as given; P and dS rounded to
-// bf16). Returns false, having done nothing, when E = f16 and this
-// workgroup's k or v does not fit f16.
+// bf16). Returns false, having written nothing, when E = f16 and this
+// workgroup's k or v does not fit f16, or one of its dS values did not.
 template <int D, bool MASK, typename E>
 __device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *sQ1, E *sO1, float *sL0, float *sD0,
                                          float *sL1, float *sD1) {
@@ -522,6 +522,10 @@ __device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *
     if constexpr (kHalf)
       if (__syncthreads_or(bad)) return false;
   }
+  // (f16 operands) the largest |dS| rounded to f16: dS = P (dP - delta) can
+  // leave the f16 range although every input fits it; the workgroup then runs
+  // again on bf16 operands
+  float ds_max = 0.f;
   f32x16 dk[ND], dv[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) { dk[i] = f32x16{}; dv[i] = f32x16{}; }
@@ -631,7 +635,9 @@ __device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *
       float ex = fast_exp2(__builtin_fmaf(sc[sub][j], sl2, -l4[sub][e]));
       if constexpr (MASK) ex = (uint32_t)(c - mlo) < mspan ? ex : 0.f;
       pb[sub][j >> 3][j & 7] = (E)ex;
-      db[sub][j >> 3][j & 7] = (E)(ex * (dpv[sub][j] - d4[sub][e]));
+      const float dsv = ex * (dpv[sub][j] - d4[sub][e]);
+      db[sub][j >> 3][j & 7] = (E)dsv;
+      if constexpr (kHalf) ds_max = fmaxf(ds_max, fabsf(dsv));
     };
     Frag fq[KS], fo[KS];  // A fragments by score step (each live for PFA steps)
     auto load_a = [&](int k) {
@@ -702,6 +708,8 @@ __device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *
     compute(sQ1, sO1, sL1, sD1);
     __syncthreads();
   }
+  if constexpr (kHalf)
+    if (__syncthreads_or(!(ds_max <= 65504.f))) return false;  // nothing written yet
   if (!key_ok) return true;
   float *dkr = p.dk + (int64_t)key * p.dk_st + (int64_t)hk * p.dk_sh;
   float *dvr = p.dv + (int64_t)key * p.dv_st + (int64_t)hk * p.dv_sh;
