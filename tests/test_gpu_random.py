@@ -22,7 +22,7 @@ from blockwise_causal_varlen_amd import inputs
 pytestmark = pytest.mark.gpu
 
 EDGE_LENS = [0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 256, 300, 511, 513, 1000]
-N_CASES = 40
+N_CASES = 200
 SENTINEL_OUT, SENTINEL_LSE = 7.0, 9.0
 
 

@@ -35,7 +35,7 @@ def check(out, lse, ro, rl, what, tol=OUT_TOL, lse_tol=LSE_TOL):
     assert e_o <= tol and e_l <= lse_tol, (what, e_o, e_l)
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(40))
 def test_random_kvp(gpu_lib, i):
     rng = np.random.default_rng(5000 + i)
     R = int(rng.choice([1, 2, 4]))
@@ -63,7 +63,7 @@ def test_random_kvp(gpu_lib, i):
     check(out, lse, ro, rl, f"kvp {i}")
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(32))
 def test_random_decode(gpu_lib, i):
     L = gpu_lib
     rng = np.random.default_rng(7000 + i)
