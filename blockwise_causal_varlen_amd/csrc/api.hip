@@ -1470,12 +1470,23 @@ static attn_mask kvp_paged_mask(const attn_mask *m) {
 // prologue and an epilogue. (KV-parallel prefill of 2048 rows x 8 heads, R = 4: 16 parts a rank -> 3: W = 0 1.30 -> 1.08 ms,
 // W = 4096 0.246 -> 0.170 ms; the merge 193 -> ~30 us.)
 constexpr int64_t kKvpItems = 1536;
+// A window bounds the keys one item's rows see on one rank: about window / R
+// with round-robin keys, up to the window with contiguous ones. A part shorter
+// than kKvpMinPartKeys only adds a prologue, an epilogue and merge reads
+// (the prefill above with W = 4096, round-robin: 3 parts -> 1 part a rank,
+// 0.173 -> 0.157 ms, the forward kernel unchanged and the merge 30 -> 16 us).
+constexpr int64_t kKvpMinPartKeys = 1024;
 // Returns the batched path's problem: kvp_all_parts(R, result) && result.gather
 // selects it, else the ranks run one by one on the unadjusted plan.
-Problem kvp_parts(int32_t R, Problem P, int32_t num_seqs) {
+Problem kvp_parts(int32_t R, Problem P, int32_t num_seqs, const attn_mask *m) {
   if (P.nseg <= 1) return P;
   const int64_t wgs = ((int64_t)P.n_q / kFwdBM + num_seqs) * P.hq * R;
   int64_t n = wgs > 0 ? (kKvpItems + wgs - 1) / wgs : 1;
+  if (m->window > 0) {
+    const int64_t span = (m->kv_interleave > 0 ? m->window / m->kv_interleave : m->window) + kFwdBM;
+    const int64_t most = span / kKvpMinPartKeys;
+    if (n > most) n = most;
+  }
   if (n < 1) n = 1;
   if (n < P.nseg) {
     P.nseg = n;
@@ -1496,7 +1507,7 @@ attn_status attn_kvp_workspace_size(int32_t R, const attn_tensor *q, const attn_
   Problem P;
   TRY(plan_fwd(q, k, k, num_seqs, max_seqlen_q, max_seqlen_k, mask, P, true, false));
   P.decode = false;
-  if (const Problem Pb = kvp_parts(R, P, num_seqs); kvp_all_parts(R, Pb) && Pb.gather) {
+  if (const Problem Pb = kvp_parts(R, P, num_seqs, mask); kvp_all_parts(R, Pb) && Pb.gather) {
     P = Pb;
     if (P.nseg == 0) P.nseg = 1;
     const size_t g = kvp_gather_bytes(R, P);
@@ -1529,7 +1540,7 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
   char *w = (char *)workspace;
   Problem P;
   TRY(plan_fwd(q, &k_caches[0], &k_caches[0], num_seqs, max_seqlen_q, max_seqlen_k, mask, P, true, false));
-  if (const Problem Pb = kvp_parts(R, P, num_seqs); kvp_all_parts(R, Pb) && Pb.gather) {
+  if (const Problem Pb = kvp_parts(R, P, num_seqs, mask); kvp_all_parts(R, Pb) && Pb.gather) {
     P = Pb;
     const int64_t n = P.nseg > 0 ? P.nseg : 1;
     const int64_t slice = P.n_q * P.hq * P.d, lslice = P.hq * P.n_q;
