@@ -748,7 +748,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
   float *arow = p.acc + (int64_t)row * p.a_st + (int64_t)h * p.a_sh;
   const int64_t lidx = (int64_t)h * p.lse_n + row;
   float ln = lse_v;
+  float4 acc4[ND][4];
   if (p.merge) {
+    // The running out rows load beside the running lse, not after it: every
+    // row a merging launch touches had its acc written by the schedule's
+    // first block, and a row whose lse is still -inf takes weight 0 below by
+    // a select, so what its acc holds never enters the result.
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        acc4[dt][j4] = *reinterpret_cast<const float4 *>(arow + dt * 32 + 8 * j4 + 4 * g);
     // online-softmax merge with the running state of this (row, head), in the
     // sigmoid form: lse' = max + log1p(exp(-|la - lb|)), sig = exp(lb - lse'),
     // out' = acc - sig (acc - block_out); an empty side has weight 0
@@ -774,9 +784,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
       float4 v4 = {o[dt][4 * j4] * wb, o[dt][4 * j4 + 1] * wb, o[dt][4 * j4 + 2] * wb, o[dt][4 * j4 + 3] * wb};
-      if (wa != 0.f) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(arow + d0);
-        v4.x += wa * a4.x; v4.y += wa * a4.y; v4.z += wa * a4.z; v4.w += wa * a4.w;
+      if (p.merge) {
+        const float4 a4 = acc4[dt][j4];
+        const bool use = wa != 0.f;
+        v4.x = use ? v4.x + wa * a4.x : v4.x;
+        v4.y = use ? v4.y + wa * a4.y : v4.y;
+        v4.z = use ? v4.z + wa * a4.z : v4.z;
+        v4.w = use ? v4.w + wa * a4.w : v4.w;
       }
       if (!fin) {
         *reinterpret_cast<float4 *>(arow + d0) = v4;
