@@ -713,16 +713,23 @@ __device__ __forceinline__ bool dkdv_run(const BwdParams &p, E *sQ0, E *sO0, E *
   if (!key_ok) return true;
   float *dkr = p.dk + (int64_t)key * p.dk_st + (int64_t)hk * p.dk_sh;
   float *dvr = p.dv + (int64_t)key * p.dv_st + (int64_t)hk * p.dv_sh;
+  // every load of the key's rows before any store (interleaved, the loads
+  // would wait for memory one by one)
+  float4 pk[ND][4], pv[ND][4];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
       const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-      if (!p.set_kv) {
-        a = *reinterpret_cast<float4 *>(dkr + d0);
-        b = *reinterpret_cast<float4 *>(dvr + d0);
-      }
+      pk[dt][j4] = p.set_kv ? float4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const float4 *>(dkr + d0);
+      pv[dt][j4] = p.set_kv ? float4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const float4 *>(dvr + d0);
+    }
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      const int d0 = dt * 32 + 8 * j4 + 4 * g;
+      float4 a = pk[dt][j4], b = pv[dt][j4];
       a.x += p.scale * dk[dt][4 * j4]; a.y += p.scale * dk[dt][4 * j4 + 1];
       a.z += p.scale * dk[dt][4 * j4 + 2]; a.w += p.scale * dk[dt][4 * j4 + 3];
       *reinterpret_cast<float4 *>(dkr + d0) = a;
@@ -921,16 +928,24 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
   }
   if (!row_ok) return;
   float *dqr = p.dq + (int64_t)row * p.dq_st + (int64_t)h * p.dq_sh;
+  // every load of the row before any store: the compiler keeps a load after
+  // an earlier store of the same row, so interleaved they would wait for
+  // memory one by one
+  float4 prev[ND][4];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+      prev[dt][j4] = p.set_q ? float4{0.f, 0.f, 0.f, 0.f}
+                             : *reinterpret_cast<const float4 *>(dqr + dt * 32 + 8 * j4 + 4 * g);
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int j4 = 0; j4 < 4; ++j4) {
-      const int d0 = dt * 32 + 8 * j4 + 4 * g;
-      float4 a = {0.f, 0.f, 0.f, 0.f};
-      if (!p.set_q) a = *reinterpret_cast<float4 *>(dqr + d0);
+      float4 a = prev[dt][j4];
       a.x += p.scale * dq[dt][4 * j4]; a.y += p.scale * dq[dt][4 * j4 + 1];
       a.z += p.scale * dq[dt][4 * j4 + 2]; a.w += p.scale * dq[dt][4 * j4 + 3];
-      *reinterpret_cast<float4 *>(dqr + d0) = a;
+      *reinterpret_cast<float4 *>(dqr + dt * 32 + 8 * j4 + 4 * g) = a;
     }
 }
 
