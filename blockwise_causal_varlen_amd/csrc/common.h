@@ -145,12 +145,16 @@ struct PosMap {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int D, int PCH> struct PadTile {
-  static constexpr int CPR = D / 8;            // data chunks per row
-  static constexpr int NBLK = PCH;             // 1 KB blocks (64 rows x PCH chunks / 64)
-  static constexpr int NJ = (NBLK + 3) / 4;    // blocks per wave (4 waves)
-  static constexpr int PITCH = PCH * 8;        // elements per row
-  static constexpr int ELEMS = 64 * PITCH;     // elements per tile
+// ROWS = 64 or 32. The copies write whole 1 KB blocks, so a tile of 32 rows
+// whose slots do not fill its last block is given room for all of it.
+template <int D, int PCH, int ROWS = 64> struct PadTile {
+  static constexpr int CPR = D / 8;                     // data chunks per row
+  static constexpr int SPR = PCH;                       // slots per row
+  static constexpr int NROWS = ROWS;
+  static constexpr int NBLK = (ROWS * PCH + 63) / 64;   // 1 KB blocks
+  static constexpr int NJ = (NBLK + 3) / 4;             // blocks per wave (4 waves)
+  static constexpr int PITCH = PCH * 8;                 // elements per row
+  static constexpr int ELEMS = NBLK * 512;              // elements of the buffer
   static constexpr bool kSwz = false;
 };
 
@@ -163,7 +167,7 @@ template <int D, int PCH> struct PadTile {
 // puts each row in its own quarter of the chunks: both are conflict free,
 // where a padded pitch can serve only one of the two patterns.
 struct SwzTile128 {
-  static constexpr int CPR = 16, NBLK = 16, NJ = 4, PITCH = 128, ELEMS = 64 * PITCH;
+  static constexpr int CPR = 16, SPR = 16, NROWS = 64, NBLK = 16, NJ = 4, PITCH = 128, ELEMS = 64 * PITCH;
   static constexpr bool kSwz = true;
 };
 __device__ __forceinline__ int swz128(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
@@ -208,9 +212,9 @@ __device__ __forceinline__ void tile_voffsets(int *voff, int64_t st, int wave, i
   for (int j = 0; j < TT::NJ; ++j) {
     const int blk = wave + 4 * j;
     const int s = blk * 64 + lane;
-    const int r = s / TT::NBLK, c = s % TT::NBLK;
+    const int r = s / TT::SPR, c = s % TT::SPR;
     const int cl = TT::kSwz ? (c ^ swz128(r)) : c;  // the logical chunk this slot holds
-    voff[j] = (blk < TT::NBLK && c < TT::CPR) ? (int)(r * st * 2) + cl * 16 : kPastEnd;
+    voff[j] = (blk < TT::NBLK && r < TT::NROWS && c < TT::CPR) ? (int)(r * st * 2) + cl * 16 : kPastEnd;
   }
 }
 

@@ -519,16 +519,16 @@ __device__ __forceinline__ const FwdParams &fwd_pick(const FwdBatch &b) { return
 // MASK = false: launches without a causal or window mask; only the keys past
 // the end of a ragged last tile are masked.
 // PT: FwdParams (one forward) or FwdBatch (grid.y picks the forward)
-template <int D, typename OutT, bool MASK, typename PT>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
+template <int D, typename OutT, bool MASK, typename PT, int BN>
+__global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args) {
   const FwdParams &p = fwd_pick(args);
   using M = Mfma32<bf16>;
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int BN = kFwdBN;
-  using KT = PadTile<D, D / 8 + 1>;  // row reads
-  using VT = PadTile<D, D / 8 + 4>;  // transpose reads
-  static_assert(BN == 64, "tiles are 64 rows");
+  constexpr int NSB = BN / 32;  // 32-key sub-tiles of a tile
+  using KT = PadTile<D, D / 8 + 1, BN>;  // row reads
+  using VT = PadTile<D, D / 8 + 4, BN>;  // transpose reads
+  static_assert(BN == 32 || BN == 64, "tiles are 32 or 64 keys");
   // A row's reference max may trail its true max by up to this much (log2
   // units) before the output is rescaled: probabilities stay <= 2^8, and the
   // final lse = max + log2(sum) is exact for any reference.
@@ -616,18 +616,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
     const bool full = (nvalid >= BN) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
     // the two 32-key sub-tiles' MFMAs alternate, so consecutive MFMAs never
     // wait on each other's accumulator
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 sc[NSB];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) sc[sb] = f32x16{};
     {
-      bf16x8 kfr[2][NS];
+      bf16x8 kfr[NSB][NS];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < NSB; ++sb)
           kfr[sb][s] = *reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + s * 16 + g * 8);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) sc[sb] = M::mma(kfr[sb][s], qf[s], sc[sb]);
+        for (int sb = 0; sb < NSB; ++sb) sc[sb] = M::mma(kfr[sb][s], qf[s], sc[sb]);
     }
     if (!full) {  // wave-uniform
       // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
@@ -636,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
       const int32_t t0 = kt - kd0 + 4 * g;
       if constexpr (!MASK) {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
@@ -645,7 +647,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
       } else if (RR == 0) {
         const int32_t d = qpos - (koff + t0), dw = d - W;  // causal: c <= d; window: c > d - W
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
           }
       } else {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
     }
     float mx = neg_inf();
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
     mx = pair32_max(mx);
@@ -680,9 +682,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
       mrow = mnew;
     }
     const float muse = mrow == neg_inf() ? 0.f : mrow;
-    bf16x8 pf[4];
+    bf16x8 pf[BN / 16];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const float e = fast_exp2(__builtin_fmaf(sc[sb][j], sl2, -muse));
@@ -692,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PT args) {
     // per 16-key chunk t: the ND d-tiles' transpose reads, then their MFMAs
     // (independent accumulators back to back)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < BN / 16; ++t) {
       bf16x8 va[ND];
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
@@ -809,11 +811,11 @@ static hipError_t launch_fwd_t(const FwdParams &fp, int out_dtype, int64_t grid,
   if constexpr (sizeof(T) == 2) {
     const bool mask = fp.m.causal || fp.m.window > 0;
     if (out_dtype == 0) {
-      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdParams, kFwdBf16BN>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdParams, kFwdBf16BN>), dim3((unsigned)grid), dim3(256), 0, s, fp);
     } else {
-      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
-      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdParams>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdParams, kFwdBf16BN>), dim3((unsigned)grid), dim3(256), 0, s, fp);
+      else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdParams, kFwdBf16BN>), dim3((unsigned)grid), dim3(256), 0, s, fp);
     }
   } else {
     if (out_dtype == 0)
@@ -858,11 +860,11 @@ template <int D>
 static hipError_t launch_fwd_batch_t(const FwdBatch &b, bool mask, int out_dtype, int64_t grid, int n, hipStream_t s) {
   const dim3 g((unsigned)grid, (unsigned)n);
   if (out_dtype == 0) {
-    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdBatch>), g, dim3(256), 0, s, b);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdBatch>), g, dim3(256), 0, s, b);
+    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, true, FwdBatch, kFwdBf16BN>), g, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, bf16, false, FwdBatch, kFwdBf16BN>), g, dim3(256), 0, s, b);
   } else {
-    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdBatch>), g, dim3(256), 0, s, b);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdBatch>), g, dim3(256), 0, s, b);
+    if (mask) hipLaunchKernelGGL((fwd_bf16_kernel<D, float, true, FwdBatch, kFwdBf16BN>), g, dim3(256), 0, s, b);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, float, false, FwdBatch, kFwdBf16BN>), g, dim3(256), 0, s, b);
   }
   return hipGetLastError();
 }

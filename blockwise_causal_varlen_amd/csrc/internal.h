@@ -46,7 +46,10 @@ struct SchedBufs {
 };
 
 constexpr int kFwdBM = 128;   // query rows per forward workgroup (4 waves x 32)
-constexpr int kFwdBN = 64;    // keys per staged tile
+constexpr int kFwdBN = 64;    // keys per staged tile (the schedule's unit of key parts)
+// keys per staged tile of the bf16 forward: 32 lets three workgroups share a
+// CU (LDS 38 KB each)
+constexpr int kFwdBf16BN = 32;
 constexpr int kBwdBQ = 64;    // query rows per staged tile of the dK/dV kernel
 constexpr int kBwdTile = 128; // query rows per dQ workgroup / key rows per dK-dV workgroup
 
