@@ -512,13 +512,15 @@ __device__ __forceinline__ const FwdParams &fwd_pick(const FwdParams &p) { retur
 __device__ __forceinline__ const FwdParams &fwd_pick(const FwdBatch &b) { return b.p[blockIdx.y]; }
 
 // bf16 forward: K/V tiles arrive by asynchronous global->LDS copies into two
-// swizzled buffers, so tile t+1 is in flight while tile t is computed; one
+// padded buffers, so tile t+1 is in flight while tile t is computed; one
 // barrier per tile. The loop is unrolled by two so that every LDS read names
 // a fixed buffer (the compiler then only waits for the copy at the barrier).
 // ---------------------------------------------------------------------------
 // MASK = false: launches without a causal or window mask; only the keys past
 // the end of a ragged last tile are masked.
 // PT: FwdParams (one forward) or FwdBatch (grid.y picks the forward)
+// BN: keys per tile; 32 (38 KB of LDS, at most 168 registers) lets three
+// workgroups share a CU, 64 fits two.
 template <int D, typename OutT, bool MASK, typename PT, int BN>
 __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args) {
   const FwdParams &p = fwd_pick(args);

@@ -46,7 +46,8 @@ struct SchedBufs {
 };
 
 constexpr int kFwdBM = 128;   // query rows per forward workgroup (4 waves x 32)
-constexpr int kFwdBN = 64;    // keys per staged tile (the schedule's unit of key parts)
+constexpr int kFwdBN = 64;    // keys per staged tile of the f32 forward and the dQ kernels; the
+                              // schedule's unit of key parts and costs
 // keys per staged tile of the bf16 forward: 32 lets three workgroups share a
 // CU (LDS 38 KB each)
 constexpr int kFwdBf16BN = 32;
