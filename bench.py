@@ -174,7 +174,8 @@ def trace_summary(stats_csv, trace_csv, bench_json, out_path, command, timed_fra
     headline bench: the stats table (every dispatch), then each library
     kernel's mean over the timed steps only (the last timed_fraction of its
     dispatches), beside the mean launch duration the bench measured live with
-    hipEvents (bench_json: the JSON line of a bench.py run of the same sources)."""
+    hipEvents (bench_json: the JSON line of a bench.py run of the same sources,
+    normally the traced run itself, so both columns time the same launches)."""
     import csv
     import statistics
     rows = list(csv.DictReader(open(stats_csv)))
