@@ -616,8 +616,9 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args
     if (causal && kp_lo > wq_hi) return;
     if (W > 0 && kp_hi <= wq_lo - W) return;
     const bool full = (nvalid >= BN) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
-    // the two 32-key sub-tiles' MFMAs alternate, so consecutive MFMAs never
-    // wait on each other's accumulator
+    // with 64-key tiles the two 32-key sub-tiles' MFMAs alternate, so
+    // consecutive MFMAs never wait on each other's accumulator; a 32-key tile
+    // is one chain, whose waits the SIMD's other waves fill
     f32x16 sc[NSB];
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) sc[sb] = f32x16{};
