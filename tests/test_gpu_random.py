@@ -67,7 +67,8 @@ def view_rows(cu, view):
     return np.asarray(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+# 503 and 602: f32 draws whose dV collects thousands of rows into one key
+@pytest.mark.parametrize("i", list(range(N_CASES)) + [503, 602])
 def test_random_block(gpu_lib, i):
     L = gpu_lib
     lens, klens, hq, hkv, d, dtype, mk = draw(i)
@@ -109,4 +110,9 @@ def test_random_block(gpu_lib, i):
         e = float(np.max(np.abs(O.as_f64(gt.cpu()) - r), initial=0.0))
         big = float(np.max(np.abs(r), initial=0.0))
         say(f"  {name}: {e:.2e} (max |ref| {big:.2f})")
-        assert e <= tol, (name, e)
+        # bf16: the stated absolute bar. f32: 1e-4 relative to the gradient's
+        # size (an f32 sum of n terms carries about sqrt(n) 2^-24 of its
+        # magnitude: one key can collect thousands of rows), capped by the
+        # stated absolute bar
+        bar = tol if dtype == torch.bfloat16 else min(2e-2, tol * max(1.0, big))
+        assert e <= bar, (name, e, bar)
