@@ -72,8 +72,10 @@ hipEvent_t pooled_event() {
     t.pool.pop_back();
     return e;
   }
+  // timestamps only: no system-scope fence around each launch (the report
+  // reads them after hipEventSynchronize)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
