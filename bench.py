@@ -215,6 +215,40 @@ def trace_summary(stats_csv, trace_csv, bench_json, out_path, command, timed_fra
     print("\n".join(lines))
 
 
+STATS_FILE = os.path.join(ROOT, "profiles", "all_rows_kernel_stats.md")
+
+
+def stats_summary(stats_csv, bench_json, out_path, command):
+    """Per-kernel statistics of a rocprofv3 --kernel-trace --stats run over the
+    whole bench (every row): calls, total and mean duration of each kernel,
+    beside the row figures the same run printed (bench_json: its JSON line)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = ["# Kernel statistics: every bench row (headline, packed varlen, KV-parallel, EAGLE-3, Ulysses, "
+             "merge, decode)", "", "Commands (from the repository root, on one MI355X):", "", "```"] + command + \
+            ["```", "", f"Sources digest {sources_digest()}. All dispatches of the profiled run, longest total first "
+             "(durations in microseconds):", "", "| kernel | calls | total us | mean us | % |",
+             "|---|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    if bench_json:
+        rec = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        lines += ["", f"The same run's bench line: headline {rec.get('value')} {rec.get('unit')}, "
+                      f"{rec.get('ms_per_step')} ms per step, sources {rec.get('sources')}. Its rows, with the "
+                      "mean launch duration of each row's measured kernel (hipEvents):", "",
+                  "| row | ms per step | kernel | mean launch us | fraction of peak |", "|---|---:|---|---:|---:|"]
+        for name, row in rec.get("rows", {}).items():
+            for sub in row.values():
+                if isinstance(sub, dict) and "mean_launch_us" in sub:
+                    lines.append(f"| {name} | {row.get('ms', 0):.4f} | {sub['kernel']} | {sub['mean_launch_us']} | "
+                                 f"{sub['frac']} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # Counters of one rocprofv3 --pmc pass each (at most 8 SQ and 2 GRBM counters a pass)
 COUNTER_PASSES = [
     ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
@@ -564,7 +598,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: turn two rocprofv3 --pmc counter CSVs into profiles/traffic.txt")
     ap.add_argument("--traffic-command", action="append", default=[],
-                    help="with --traffic-summary / --counter-summary / --trace-summary: a command line to record in the summary")
+                    help="with --traffic-summary / --counter-summary / --trace-summary / --stats-summary: a command line "
+                         "to record in the summary")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="host only: turn rocprofv3 --pmc counter CSVs (the passes of COUNTER_PASSES) into "
                          "the counter summary under profiles/")
@@ -572,6 +607,9 @@ def main():
                     help="host only: turn a rocprofv3 --kernel-trace --stats run of the headline (its "
                          "kernel_stats and kernel_trace CSVs) and a bench.py JSON line into the kernel-trace "
                          "summary under profiles/ (BENCH_JSON may be '-')")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                    help="host only: turn a rocprofv3 --kernel-trace --stats run of the whole bench (its "
+                         "kernel_stats CSV) and that run's JSON line into the all-rows summary under profiles/")
     ap.add_argument("--trace-timed-fraction", type=float, default=0.75,
                     help="with --trace-summary: the share of each kernel's dispatches in the timed steps")
     ap.add_argument("--print-counter-passes", action="store_true",
@@ -583,6 +621,10 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args.counter_summary, COUNTERS_FILE, args.traffic_command)
+        return
+    if args.stats_summary:
+        st, bj = args.stats_summary
+        stats_summary(st, None if bj == "-" else bj, STATS_FILE, args.traffic_command)
         return
     if args.trace_summary:
         st, tr, bj = args.trace_summary
