@@ -638,7 +638,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the virtual-rank schedules run all ranks on a single device and "
-              "there is no multi-GPU path in this build (--gpus 1).", file=sys.stderr)
+              "the library has no multi-GPU path (--gpus 1).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
