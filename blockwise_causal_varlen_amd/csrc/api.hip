@@ -159,6 +159,21 @@ MaskDev mask_dev(const attn_mask *m) {
 
 TensorDev tdev(const attn_tensor *t) { return TensorDev{t->data, t->stride_tok, t->stride_head}; }
 
+// Document-local key rows [lo, hi) that some query of a call can see: every
+// query position lies in [q_pos_offset, q_pos_offset + max_q), so causality
+// ends the range and a window starts it. The scheduler's per-item key ranges
+// (and so every tile the forward reads) lie inside it, so a paged gather
+// copies only these rows.
+static void visible_key_rows(const attn_mask *m, int64_t max_q, int64_t max_k, int64_t &lo, int64_t &hi) {
+  const MaskDev md = mask_dev(m);
+  lo = 0;
+  hi = max_k;
+  if (md.causal) hi = md.pm.count_le(md.q_pos_offset + max_q - 1, max_k);
+  if (md.window > 0) lo = md.pm.count_le(md.q_pos_offset - md.window, max_k);
+}
+
+
+
 // The kernels index rows, positions and in-tile offsets in 32 bits.
 static attn_status check_ranges(const attn_tensor *q, const attn_tensor *k, const attn_tensor *v,
                                 const attn_mask *m, int64_t n_k_logical) {
@@ -489,6 +504,8 @@ attn_status block_fwd_impl(const attn_tensor *q, const attn_tensor *k, const att
     ga.shift = __builtin_ctz((unsigned)mask->block_size);
     ga.dst_k = gk; ga.dst_v = gk + gb;
     ga.n_rows = P.n_k_logical; ga.h = (int32_t)P.hkv; ga.d = (int32_t)P.d; ga.eb = esize(k->dtype);
+    ga.cu = cu_seqlens_k; ga.num_seqs = num_seqs;
+    visible_key_rows(mask, max_seqlen_q, max_seqlen_k, ga.t_lo, ga.t_hi);
     TRY(hip_check(timed("attn_gather", s, [&] { return launch_page_gather(ga, s); }), "page gather"));
     kg = *k;
     kg.data = gk; kg.n_tok = P.n_k_logical; kg.stride_head = P.d; kg.stride_tok = P.hkv * P.d;
@@ -1577,6 +1594,8 @@ attn_status attn_kvp_fwd(int32_t R, const attn_tensor *q, const attn_tensor *k_c
       g.shift = __builtin_ctz((unsigned)mask->block_size);
       g.dst_k = gw + (size_t)r * 2 * gb; g.dst_v = gw + ((size_t)r * 2 + 1) * gb;
       g.n_rows = P.n_k_logical; g.h = (int32_t)P.hkv; g.d = (int32_t)P.d; g.eb = esize(kc->dtype);
+      g.cu = cu_seqlens_k; g.num_seqs = num_seqs;
+      visible_key_rows(&mr[r], max_seqlen_q, max_seqlen_k, g.t_lo, g.t_hi);
       kg[r] = *kc;
       kg[r].data = g.dst_k; kg[r].n_tok = P.n_k_logical; kg[r].stride_head = P.d; kg[r].stride_tok = P.hkv * P.d;
       vg[r] = kg[r];

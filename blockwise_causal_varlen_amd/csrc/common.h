@@ -110,7 +110,7 @@ struct PosMap {
   int32_t rank;
   int32_t block;       // B
   int32_t shift;       // log2(B) (B is a power of two when R > 0)
-  __device__ __forceinline__ int64_t kpos(int64_t t) const {
+  __host__ __device__ __forceinline__ int64_t kpos(int64_t t) const {
     if (interleave == 0) return k_pos_offset + t;
     int64_t b = t / block, o = t - b * block;
     return k_pos_offset + (b * interleave + rank) * block + o;
@@ -123,7 +123,7 @@ struct PosMap {
     return k_pos_offset + ((b * interleave + rank) * block + (t - b * block));
   }
   // Number of keys t in [0, n) with kpos(t) <= p (monotone inverse).
-  __device__ __forceinline__ int64_t count_le(int64_t p, int64_t n) const {
+  __host__ __device__ __forceinline__ int64_t count_le(int64_t p, int64_t n) const {
     int64_t lo = 0, hi = n;  // answer in [lo, hi]
     while (lo < hi) {
       int64_t mid = (lo + hi) >> 1;

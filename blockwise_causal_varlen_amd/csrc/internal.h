@@ -160,6 +160,11 @@ struct PageGatherArgs {
   void *dst_k, *dst_v;
   int64_t n_rows;
   int32_t h, d, eb;
+  // when cu is set, only the rows whose document-local index lies in
+  // [t_lo, t_hi) are copied (cu: the documents' first logical key rows)
+  const int32_t *cu;
+  int32_t num_seqs;
+  int64_t t_lo, t_hi;
 };
 hipError_t launch_page_gather(const PageGatherArgs &a, hipStream_t s);
 constexpr int kMaxGatherBatch = 16;

@@ -665,6 +665,7 @@ hipError_t launch_zigzag_shard(const void *src, int64_t s_st, int64_t s_sh, int6
 // logical key row t of a paged cache sits at page table[t >> shift], row
 // t & (2^shift - 1) of it. One wave copies one logical row (all heads, K and V)
 // into contiguous [rows, H, D] buffers; rows of an invalid page read as zero.
+// With a visible range (a.cu set) only the rows some query can see are copied.
 // ---------------------------------------------------------------------------
 __device__ void page_gather_run(const PageGatherArgs &a) {
   const int lane = threadIdx.x & 63;
@@ -678,6 +679,16 @@ __device__ void page_gather_run(const PageGatherArgs &a) {
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t step = (int64_t)gridDim.x * 4 * rpw;
   for (int64_t t = wave * rpw + lane / lpr; t < a.n_rows; t += step) {
+    if (a.cu) {  // rows no query of the call sees are left alone (nothing reads them)
+      if (a.num_seqs <= 0 || t < a.cu[0] || t >= a.cu[a.num_seqs]) continue;
+      int lo = 0, hi = a.num_seqs;  // cu[lo] <= t < cu[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      const int64_t tl = t - a.cu[lo];
+      if (tl < a.t_lo || tl >= a.t_hi) continue;
+    }
     const int64_t b = t >> a.shift;
     const int64_t pg = b < a.max_blocks ? a.table[b] : -1;
     const bool ok = pg >= 0 && pg < a.n_pages;
