@@ -60,8 +60,8 @@ __all__ = [
 # ----------------------------------------------------------------------------
 def as_f64(x) -> np.ndarray:
     """Exact upcast to float64 (bf16 and fp32 values are representable)."""
-    if hasattr(x, "detach"):  # a torch tensor; .float() widens bf16 exactly
-        x = x.detach().to("cpu").float().numpy()
+    if hasattr(x, "detach"):  # a torch tensor: .double() widens bf16, f16, f32 exactly and keeps f64
+        x = x.detach().to("cpu").double().numpy()
     return np.asarray(x, dtype=np.float64)
 
 
