@@ -531,10 +531,17 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args
   using KT = PadTile<D, D / 8 + 1, BN>;  // row reads
   using VT = PadTile<D, D / 8 + 4, BN>;  // transpose reads
   static_assert(BN == 32 || BN == 64, "tiles are 32 or 64 keys");
-  // A row's reference max may trail its true max by up to this much (log2
-  // units) before the output is rescaled: probabilities stay <= 2^8, and the
-  // final lse = max + log2(sum) is exact for any reference.
+  // A row's reference max may trail its true max: the final lse = max +
+  // log2(sum) is exact for any reference, and f32 and bf16 keep the same
+  // relative precision at any magnitude. Once every row of a wave has a
+  // reference, a tile's probabilities are formed against it without the
+  // tile's max; they are kept unless some row's share of the tile sum passes
+  // 2^kTileSumLog2 (its max outgrew the reference by at least that much less
+  // log2(16)). Otherwise, or while a row has no reference, the tile's max is
+  // taken, and the output rescaled when it passes the reference by more than
+  // kRescaleSlack.
   constexpr float kRescaleSlack = 8.f;
+  constexpr float kTileSumMax = 4294967296.f;  // 2^32
   __shared__ __attribute__((aligned(1024))) bf16 sK0[KT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sV0[VT::ELEMS];
   __shared__ __attribute__((aligned(1024))) bf16 sK1[KT::ELEMS];
@@ -669,31 +676,43 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args
           }
       }
     }
-    float mx = neg_inf();
-#pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
-    mx = pair32_max(mx);
-    const float mt = mx * sl2;
-    if (!__all(mt <= mrow + kRescaleSlack)) {  // some row outgrew its reference
-      const float mnew = fmaxf(mrow, mt);
-      const float alpha = fast_exp2(mrow - (mnew == neg_inf() ? 0.f : mnew));
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < ND; ++i) o[i] *= alpha;
-      mrow = mnew;
-    }
-    const float muse = mrow == neg_inf() ? 0.f : mrow;
     bf16x8 pf[BN / 16];
+    float ts = 0.f;  // this lane's share of the tile's row sum
+    auto probs = [&](float ref) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float e = fast_exp2(__builtin_fmaf(sc[sb][j], sl2, -muse));
-        lsum += e;
-        pf[sb * 2 + (j >> 3)][j & 7] = (bf16)e;
+        for (int j = 0; j < 16; ++j) {
+          const float e = fast_exp2(__builtin_fmaf(sc[sb][j], sl2, -ref));
+          ts = (sb | j) ? ts + e : e;
+          pf[sb * 2 + (j >> 3)][j & 7] = (bf16)e;
+        }
+    };
+    // wave-uniform: a NaN or infinite share fails the test as well
+    bool kept = false;
+    if (__all(mrow != neg_inf())) {
+      probs(mrow);
+      kept = __all(ts <= kTileSumMax);
+    }
+    if (!kept) {
+      float mx = neg_inf();
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[sb][j]);
+      mx = pair32_max(mx);
+      const float mt = mx * sl2;
+      if (!__all(mt <= mrow + kRescaleSlack)) {  // some row outgrew its reference
+        const float mnew = fmaxf(mrow, mt);
+        const float alpha = fast_exp2(mrow - (mnew == neg_inf() ? 0.f : mnew));
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) o[i] *= alpha;
+        mrow = mnew;
       }
+      probs(mrow == neg_inf() ? 0.f : mrow);
+    }
+    lsum += ts;
     // per 16-key chunk t: the ND d-tiles' transpose reads, then their MFMAs
     // (independent accumulators back to back)
 #pragma unroll

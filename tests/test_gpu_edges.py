@@ -230,3 +230,33 @@ def test_bwd_values_beyond_f16_range(gpu_lib, where):
     for name, g in zip(("dq", "dk", "dv"), got):
         assert torch.isfinite(g).all(), f"{name}: non-finite values"
     check_bwd(got, rb, f"beyond f16 {where}", rel=2.0 ** -8)
+
+
+@pytest.mark.parametrize("growth", [-20.0, 20.0, 60.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_that_grow_along_the_keys(gpu_lib, growth, causal):
+    """Scores that rise (or fall) by `growth` log2 units per 32 keys along each
+    document, so that a row's running max moves far between key tiles: at 20
+    the forward keeps a stale reference (probabilities up to 2^20 and more),
+    at 60 every tile passes it by more than its tile-sum bound and is
+    redone with its own max, at -20 the first tile holds every row's max."""
+    L = gpu_lib
+    lens = [200, 150]  # scores stay within a few hundred (f32 keeps the lse bar)
+    hq, hkv, d = 2, 1, 128
+    g = torch.Generator().manual_seed(71)
+    cu = inputs.cu_from_lengths(lens)
+    n = int(cu[-1])
+    scale = 1.0 / math.sqrt(d)
+    # q ~ 1 and k_j ~ a_j: score_j ~ sqrt(d) a_j, i.e. sqrt(d) log2(e) a_j log2 units
+    per_key = growth / 32.0 / (math.sqrt(d) * math.log2(math.e))
+    pos = torch.cat([torch.arange(L_, dtype=torch.float32) for L_ in lens])
+    a = per_key * (pos - (pos.max() if growth < 0 else 0.0))
+    q = (1.0 + 0.1 * torch.randn(n, hq, d, generator=g)).to(torch.bfloat16)
+    k = (a[:, None, None] * (1.0 + 0.1 * torch.randn(n, hkv, d, generator=g))).to(torch.bfloat16)
+    v = torch.randn(n, hkv, d, generator=g).to(torch.bfloat16)
+    mk = dict(causal=causal)
+    say(f"growth {growth} causal {causal}")
+    ro, rl = O.block_forward(q, k, v, cu, cu, scale, **mk)
+    out, lse = L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu, cu, max(lens), max(lens), scale, L.mask(**mk))
+    torch.cuda.synchronize()
+    check_fwd(out, lse, ro, rl, f"growth {growth} causal {causal}")
