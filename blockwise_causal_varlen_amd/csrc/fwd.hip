@@ -636,6 +636,10 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
           kfr[sb][s] = *reinterpret_cast<const bf16x8 *>(sk + (sb * 32 + l32) * KT::PITCH + s * 16 + g * 8);
+      // every K read is issued before the first MFMA (left alone, the
+      // compiler issues them two at a time, each pair waited for just before
+      // its MFMAs): 304 -> 302 us a launch on the headline step
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
