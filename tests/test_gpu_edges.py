@@ -2,9 +2,10 @@
 fp64 oracle: calls with no documents, empty tensors, documents whose query or
 key side is empty, query rows that see no key, MHA and 16-way GQA, the decode
 kernel at its GQA limit and the tiled path beyond it, and windows of one key
-or longer than any document. Rows that see nothing must come back as out 0,
-lse -inf, with zero gradients; calls with no work must leave every output as
-the caller left it.
+or longer than any document, and scores that move by tens of log2 units
+between key tiles (the forward's running reference). Rows that see nothing
+must come back as out 0, lse -inf, with zero gradients; calls with no work
+must leave every output as the caller left it.
 """
 
 import math
@@ -260,3 +261,33 @@ def test_scores_that_grow_along_the_keys(gpu_lib, growth, causal):
     out, lse = L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu, cu, max(lens), max(lens), scale, L.mask(**mk))
     torch.cuda.synchronize()
     check_fwd(out, lse, ro, rl, f"growth {growth} causal {causal}")
+
+
+@pytest.mark.parametrize("seed", [81, 82, 83])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_on_a_random_walk(gpu_lib, seed, d):
+    """Scores that follow a random walk along the keys (steps of up to tens of
+    log2 units per key tile, up and down), different for every kv head, with
+    GQA and ragged documents: a row's running reference trails, catches up
+    with, and overshoots its true max in turn."""
+    L = gpu_lib
+    g = torch.Generator().manual_seed(seed)
+    lens = [int(x) for x in torch.randint(40, 260, (3,), generator=g)]
+    hq, hkv = 4, 2
+    cu = inputs.cu_from_lengths(lens)
+    n = int(cu[-1])
+    scale = 1.0 / math.sqrt(d)
+    log2_per_unit = math.sqrt(d) * math.log2(math.e)  # q ~ 1, k ~ a: score ~ sqrt(d) a
+    steps = torch.randn(n, hkv, generator=g) * (12.0 / log2_per_unit)
+    a = torch.cumsum(steps, dim=0)
+    a = a - a.mean()
+    q = (1.0 + 0.1 * torch.randn(n, hq, d, generator=g)).to(torch.bfloat16)
+    k = (a[:, :, None] * (1.0 + 0.1 * torch.randn(n, hkv, d, generator=g))).to(torch.bfloat16)
+    v = torch.randn(n, hkv, d, generator=g).to(torch.bfloat16)
+    for causal in (False, True):
+        mk = dict(causal=causal)
+        say(f"random walk seed {seed} d {d} lens {lens} causal {causal}")
+        ro, rl = O.block_forward(q, k, v, cu, cu, scale, **mk)
+        out, lse = L.block_fwd(q.cuda(), k.cuda(), v.cuda(), cu, cu, max(lens), max(lens), scale, L.mask(**mk))
+        torch.cuda.synchronize()
+        check_fwd(out, lse, ro, rl, f"random walk seed {seed} d {d} causal {causal}")
