@@ -15,9 +15,10 @@
 // the 32x32 MFMA so that a lane owns one query row (lane % 32) and 16 keys of
 // every 32-key sub-tile: the row max needs one exchange with lane ^ 32, the
 // exponentiated scores are already in the register layout of the B operand of
-// O^T += V^T P^T, and the output rescale is a per-lane scalar. K and V tiles of
-// 64 keys are staged through LDS; V^T operands are read with the gfx950 LDS
-// transpose read (ds_read_b64_tr_b16), K with 16-byte reads on a padded pitch.
+// O^T += V^T P^T, and the output rescale is a per-lane scalar. K and V tiles
+// (32 keys in the bf16 kernel, 64 in the f32 one) are staged through LDS; V^T
+// operands are read with the gfx950 LDS transpose read (ds_read_b64_tr_b16), K
+// with 16-byte reads on a padded pitch.
 #include "internal.h"
 
 namespace attn {
