@@ -536,9 +536,9 @@ __global__ __launch_bounds__(256, BN == 32 ? 3 : 2) void fwd_bf16_kernel(PT args
   // log2(sum) is exact for any reference, and f32 and bf16 keep the same
   // relative precision at any magnitude. Once every row of a wave has a
   // reference, a tile's probabilities are formed against it without the
-  // tile's max; they are kept unless some row's share of the tile sum passes
-  // 2^kTileSumLog2 (its max outgrew the reference by at least that much less
-  // log2(16)). Otherwise, or while a row has no reference, the tile's max is
+  // tile's max; they are kept unless some lane's share of a row's tile sum
+  // passes 2^32 (the row's max outgrew the reference by at least 32 - log2(16)
+  // log2 units). Otherwise, or while a row has no reference, the tile's max is
   // taken, and the output rescaled when it passes the reference by more than
   // kRescaleSlack.
   constexpr float kRescaleSlack = 8.f;
