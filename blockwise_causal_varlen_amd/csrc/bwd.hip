@@ -22,6 +22,7 @@
 
 #include "internal.h"
 
+
 namespace attn {
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -857,61 +858,65 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
     if (causal && kp_lo > wq_hi) return;
     if (W > 0 && kp_hi <= wq_lo - W) return;
     const bool full = (nvalid >= KB) && (!causal || kp_hi <= wq_lo) && (W <= 0 || kp_lo > wq_hi - W);
-    f32x16 s[2], dp[2];
+    // One 32-key half at a time: its S and dP, dS, and its dQ MFMAs, so that
+    // only one half's S and dP are live; the registers this frees hold the K
+    // and V fragments kRA k-steps ahead of their MFMAs (the compiler would
+    // otherwise read each one just before its MFMA). attn_dq 432-434 -> 419-420
+    // us a launch on the zig-zag cp=8 rank-3 step (two alternating runs on one
+    // box); the halves alone gave about a third of that.
+    constexpr int kRA = 3;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-      s[sb] = f32x16{};
-      dp[sb] = f32x16{};
+      f32x16 s1 = f32x16{}, dp1 = f32x16{};
+      bf16x8 kfr[NS], vfr[NS];
+      auto rd = [&](int st) {
+        const int koff_ = KT::kSwz ? sb * 32 * 128 + ro[st] : (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8;
+        kfr[st] = *reinterpret_cast<const bf16x8 *>(sk + koff_);
+        vfr[st] = *reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8);
+      };
+#pragma unroll
+      for (int st = 0; st < kRA; ++st) rd(st);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
-        const int koff_ = KT::kSwz ? sb * 32 * 128 + ro[st] : (sb * 32 + l32) * KT::PITCH + st * 16 + g * 8;
-        s[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sk + koff_), qf[st], s[sb]);
-        dp[sb] = M::mma(*reinterpret_cast<const bf16x8 *>(sv + (sb * 32 + l32) * VT::PITCH + st * 16 + g * 8), of[st], dp[sb]);
+        if (st + kRA < NS) rd(st + kRA);
+        s1 = M::mma(kfr[st], qf[st], s1);
+        dp1 = M::mma(vfr[st], of[st], dp1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    float ds[2][16];
+      float ds1[16];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) ds[sb][j] = fast_exp2(__builtin_fmaf(s[sb][j], sl2, -lrow)) * (dp[sb][j] - drow);
-    if (!full) {  // wave-uniform
-      // element (sb, j) holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
-      const int32_t lim = nvalid - 4 * g;
-      const int32_t t0 = kt - kd0 + 4 * g;
-      if constexpr (!MASK) {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+      for (int j = 0; j < 16; ++j) ds1[j] = fast_exp2(__builtin_fmaf(s1[j], sl2, -lrow)) * (dp1[j] - drow);
+      if (!full) {  // wave-uniform
+        // element j holds key kt + 4g + c, c = 32 sb + 8 (j / 4) + j % 4
+        const int32_t lim = nvalid - 4 * g;
+        const int32_t t0 = kt - kd0 + 4 * g;
+        if constexpr (!MASK) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
-            ds[sb][j] = c < lim ? ds[sb][j] : 0.f;
+            ds1[j] = c < lim ? ds1[j] : 0.f;
           }
-      } else if (RR == 0) {
-        const int32_t d = qpos - (koff + t0), dw = d - W;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        } else if (RR == 0) {
+          const int32_t d = qpos - (koff + t0), dw = d - W;
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
             const bool vis = (c < lim) & ((causal == 0) | (c <= d)) & ((W <= 0) | (c > dw));
-            ds[sb][j] = vis ? ds[sb][j] : 0.f;
+            ds1[j] = vis ? ds1[j] : 0.f;
           }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        } else {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int c = sb * 32 + 8 * (j >> 2) + (j & 3);
             const int32_t kpj = kpos_rr(t0 + c);
             const bool vis = (c < lim) & ((causal == 0) | (kpj <= qpos)) & ((W <= 0) | (kpj > qpos - W));
-            ds[sb][j] = vis ? ds[sb][j] : 0.f;
+            ds1[j] = vis ? ds1[j] : 0.f;
           }
+        }
       }
-    }
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if constexpr (KT::kSwz) acc_transposed_swz<ND>(dq, sk, sb * 32, trl, trh, ds[sb]);
-      else acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds[sb], lane);
+      if constexpr (KT::kSwz) acc_transposed_swz<ND>(dq, sk, sb * 32, trl, trh, ds1);
+      else acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds1, lane);
     }
   };
 
