@@ -134,6 +134,21 @@ __device__ __forceinline__ void acc_transposed_all(f32x16 (&acc)[ND], const bf16
   }
 }
 
+// The ND transposed A fragments (d rows dt*32.., k = the 16 tile rows from
+// blk) of a SwzTile128 (offsets from swz_tr_offsets).
+template <int ND>
+__device__ __forceinline__ void swz_tr_frags(bf16x8 (&a)[ND], const bf16 *blk, const int (&lo)[ND],
+                                             const int (&hi)[ND]) {
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) {
+    i16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + lo[dt]));
+    i16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + hi[dt]));
+    bf16x4 l4 = __builtin_bit_cast(bf16x4, l), h4 = __builtin_bit_cast(bf16x4, h);
+    a[dt][0] = l4[0]; a[dt][1] = l4[1]; a[dt][2] = l4[2]; a[dt][3] = l4[3];
+    a[dt][4] = h4[0]; a[dt][5] = h4[1]; a[dt][6] = h4[2]; a[dt][7] = h4[3];
+  }
+}
+
 // acc_transposed_all on a SwzTile128 (offsets from swz_tr_offsets; r0 a
 // multiple of 16).
 template <int ND>
@@ -144,16 +159,8 @@ __device__ __forceinline__ void acc_transposed_swz(f32x16 (&acc)[ND], const bf16
     bf16x8 b;
 #pragma unroll
     for (int e = 0; e < 8; ++e) b[e] = (bf16)pv[t * 8 + e];
-    const bf16 *blk = base + (r0 + t * 16) * 128;
     bf16x8 a[ND];
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      i16x4 l = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + lo[dt]));
-      i16x4 h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(blk + hi[dt]));
-      bf16x4 l4 = __builtin_bit_cast(bf16x4, l), h4 = __builtin_bit_cast(bf16x4, h);
-      a[dt][0] = l4[0]; a[dt][1] = l4[1]; a[dt][2] = l4[2]; a[dt][3] = l4[3];
-      a[dt][4] = h4[0]; a[dt][5] = h4[1]; a[dt][6] = h4[2]; a[dt][7] = h4[3];
-    }
+    swz_tr_frags<ND>(a, base + (r0 + t * 16) * 128, lo, hi);
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) acc[dt] = Mfma32<bf16>::mma(a[dt], b, acc[dt]);
   }
@@ -884,6 +891,13 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
         dp1 = M::mma(vfr[st], of[st], dp1);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the K^T fragments of the half's first 16 keys, read before dS is
+      // formed so that their latency hides under it: 417-419 -> 414-415 us
+      bf16x8 ta[ND];
+      if constexpr (KT::kSwz) {
+        swz_tr_frags<ND>(ta, sk + sb * 32 * 128, trl, trh);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       float ds1[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) ds1[j] = fast_exp2(__builtin_fmaf(s1[j], sl2, -lrow)) * (dp1[j] - drow);
@@ -915,8 +929,21 @@ __global__ __launch_bounds__(256, 2) void dq_bf16_kernel(BwdParams p) {
           }
         }
       }
-      if constexpr (KT::kSwz) acc_transposed_swz<ND>(dq, sk, sb * 32, trl, trh, ds1);
-      else acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds1, lane);
+      if constexpr (KT::kSwz) {
+        bf16x8 b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (bf16)ds1[e];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dq[dt] = M::mma(ta[dt], b, dq[dt]);
+        bf16x8 tb[ND];
+        swz_tr_frags<ND>(tb, sk + (sb * 32 + 16) * 128, trl, trh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = (bf16)ds1[8 + e];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dq[dt] = M::mma(tb[dt], b, dq[dt]);
+      } else {
+        acc_transposed_all<ND>(dq, sk, KT::PITCH, sb * 32, ds1, lane);
+      }
     }
   };
 
